@@ -1,0 +1,184 @@
+"""ctypes binding of ``libq4w.so`` -- argument marshalling only.
+
+Every function takes torch tensors on the GPU, checks nothing the library
+does not check itself beyond dtype/contiguity, and hands raw device pointers
+plus torch's current HIP stream to the C ABI (``include/q4w.h``).  There is
+no fallback: if the library is missing the call raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libq4w.so"
+_lib = None
+
+STATUS = {
+    0: "OK",
+    -1: "INVALID_ARG",
+    -2: "UNSUPPORTED_SHAPE",
+    -3: "MISALIGNED",
+    -4: "WORKSPACE",
+    -5: "HIP",
+}
+
+
+class Q4WError(RuntimeError):
+    def __init__(self, fn, status, hip_err=0):
+        self.status = status
+        self.hip_error = hip_err
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}"
+                         + (f" (hipError {hip_err})" if status == -5 else ""))
+
+
+def lib_path():
+    return os.path.join(_HERE, "lib", LIB_NAME)
+
+
+def lib():
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.q4_pack.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.q4_pack.restype = i32
+    L.q4_gemv_skinny_ws_bytes.argtypes = [i32, i64, i64, i32]
+    L.q4_gemv_skinny_ws_bytes.restype = sz
+    L.q4_gemv_skinny.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, sz, vp]
+    L.q4_gemv_skinny.restype = i32
+    L.a8_quantize_act.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.a8_quantize_act.restype = i32
+    L.a8w4_ws_bytes.argtypes = [i64, i64]
+    L.a8w4_ws_bytes.restype = sz
+    L.a8w4_gemm_prefill.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    L.a8w4_gemm_prefill.restype = i32
+    L.a8w4_debug_block_acc.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    L.a8w4_debug_block_acc.restype = i32
+    L.q4w_status_str.argtypes = [i32]
+    L.q4w_status_str.restype = ctypes.c_char_p
+    L.q4w_last_hip_error.argtypes = []
+    L.q4w_last_hip_error.restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn, st):
+    if st != 0:
+        raise Q4WError(fn, st, lib().q4w_last_hip_error() if st == -5 else 0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+# Workspaces are cached per (device, size) so repeated calls do not allocate.
+_ws_cache = {}
+
+
+def _workspace(nbytes, device, key):
+    import torch
+    if nbytes == 0:
+        return None
+    k = (key, str(device))
+    buf = _ws_cache.get(k)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[k] = buf
+    return buf
+
+
+def pack(w):
+    """fp32 W [N, K] (CUDA) -> (codes uint8 [N, K/2], scales fp16 [N, K/32])."""
+    import torch
+    _need(w, torch.float32, "w")
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 32), dtype=torch.float16, device=w.device)
+    _check("q4_pack", lib().q4_pack(_ptr(w), n, k, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def gemv_ws_bytes(m, n, k, split_k=0):
+    return lib().q4_gemv_skinny_ws_bytes(m, n, k, split_k)
+
+
+def q4_gemv_skinny_raw(x, codes, scales, y, split_k=0, ws=None):
+    """Direct call into q4_gemv_skinny with caller-provided output (no allocation)."""
+    m, k = x.shape
+    n = codes.shape[0]
+    nb = gemv_ws_bytes(m, n, k, split_k)
+    if ws is None:
+        ws = _workspace(nb, x.device, "gemv")
+    _check("q4_gemv_skinny", lib().q4_gemv_skinny(
+        _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, split_k,
+        _ptr(ws), nb, _stream()))
+    return y
+
+
+def gemv(x, codes, scales, split_k=0):
+    """fp16 X [M<=8, K] against packed weights -> fp16 Y [M, N]."""
+    import torch
+    _need(x, torch.float16, "x")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float16, "scales")
+    y = torch.empty((x.shape[0], codes.shape[0]), dtype=torch.float16, device=x.device)
+    return q4_gemv_skinny_raw(x, codes, scales, y, split_k)
+
+
+def a8_quantize_act(x):
+    """fp16 X [M, K] -> (xq int8 [M, K], sa fp32 [M, K/64]) in the canonical layout."""
+    import torch
+    _need(x, torch.float16, "x")
+    m, k = x.shape
+    xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    sa = torch.empty((m, k // 64), dtype=torch.float32, device=x.device)
+    _check("a8_quantize_act", lib().a8_quantize_act(_ptr(x), m, k, _ptr(xq), _ptr(sa), _stream()))
+    return xq, sa
+
+
+def a8w4_ws_bytes(m, k):
+    return lib().a8w4_ws_bytes(m, k)
+
+
+def a8w4_gemm(x, codes, scales, y=None):
+    """A8 prefill route: fp16 X [M, K] -> fp16 Y [M, N]."""
+    import torch
+    _need(x, torch.float16, "x")
+    m, k = x.shape
+    n = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    nb = a8w4_ws_bytes(m, k)
+    ws = _workspace(nb, x.device, "a8")
+    _check("a8w4_gemm_prefill", lib().a8w4_gemm_prefill(
+        _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, _ptr(ws), nb, _stream()))
+    return y
+
+
+def a8w4_debug_block_acc(x, codes, scales):
+    """Exact int32 block sums [M, N, K/32] from the A8 kernel's debug epilogue."""
+    import torch
+    _need(x, torch.float16, "x")
+    m, k = x.shape
+    n = codes.shape[0]
+    acc = torch.empty((m, n, k // 32), dtype=torch.int32, device=x.device)
+    nb = a8w4_ws_bytes(m, k)
+    ws = _workspace(nb, x.device, "a8")
+    _check("a8w4_debug_block_acc", lib().a8w4_debug_block_acc(
+        _ptr(x), _ptr(codes), _ptr(acc), m, n, k, _ptr(ws), nb, _stream()))
+    return acc

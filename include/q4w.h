@@ -1,0 +1,142 @@
+/*
+ * q4w.h -- C ABI of the MI355X (gfx950) 4-bit block-quantized weight matmul.
+ *
+ * Three operations, each from the pages on 4-bit LLM inference:
+ *
+ *   q4_pack            weight quantization into the 4-bit block format.
+ *                      "Qwen3.8-27B at 256K on a 24GB RTX PRO 4000 SFF"
+ *                      (page 3), the paragraph naming the public Q4_0 GGUF.
+ *   q4_gemv_skinny     the weight-streaming matmul of decode and of
+ *                      speculative verification (M = 1 + drafted tokens).
+ *                      Same page, the paragraph on decode streaming the
+ *                      quantized weights on every step, and the MTP
+ *                      n_max = 3 result (an M = 4 verify).
+ *   a8w4_gemm_prefill  the A8 prefill route: int8 activations per token per
+ *                      64 channels against the 4-bit weights in an int8
+ *                      matrix-core contraction.  "Qwen3.8-27B on RTX 4090:
+ *                      5,000 tok/s Prefill Reproduced" (page 5), section
+ *                      "Why the A8 artifact matters".
+ *
+ * Format (the pages name it but do not define it; this is the reading used):
+ *   W is [N, K] fp32, row n = output n, K = reduction width.  Y = X . What^T.
+ *   Blocks of 32 consecutive weights along K.  Per block an fp16 scale
+ *   d = fp16_RNE(fl32(absmax / 7)) and codes
+ *   q = clamp(round_half_away(fl32(w / d)), -8, 7), all 0 when d == 0.
+ *   codes  : uint8 [N, K/2] row-major; byte j of row n holds code 2j in its
+ *            low nibble and code 2j+1 in its high nibble, two's complement.
+ *   scales : fp16 bit patterns, uint16 [N, K/32] row-major.
+ *   What[n, k] = q[n, k] * d[n, k / 32].
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or equivalent),
+ *     owned by the caller; the library never allocates or frees memory and
+ *     keeps no state besides a per-thread copy of the last HIP error.
+ *   - Half-precision values cross the ABI as uint16_t bit patterns.
+ *   - `stream` is the caller's HIP stream (NULL = default stream).  Each call
+ *     only enqueues work and returns; results are valid once the stream is
+ *     synchronized, and inputs must stay alive until then.
+ *   - All argument checks run on the host before any HIP call; a failed check
+ *     returns a negative status and enqueues nothing.  No C++ exception
+ *     crosses the ABI.
+ *   - Preconditions that are NOT checked (they would need a device sync):
+ *     weights finite with |w| <= 7 * 65504, activations finite.
+ *   - Calls that share a workspace must not overlap in time (they race).
+ */
+#ifndef Q4W_H
+#define Q4W_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued entry point. */
+#define Q4W_OK                     0
+#define Q4W_ERR_INVALID_ARG       -1  /* null pointer, negative size, bad split_k */
+#define Q4W_ERR_UNSUPPORTED_SHAPE -2  /* M, K outside what the route supports */
+#define Q4W_ERR_MISALIGNED        -3  /* a pointer violates the stated alignment */
+#define Q4W_ERR_WORKSPACE         -4  /* workspace missing or smaller than required */
+#define Q4W_ERR_HIP               -5  /* a HIP call failed; see q4w_last_hip_error() */
+
+/*
+ * q4_pack: quantize fp32 weights into codes + scales (format above).
+ *   w      [N, K] fp32, 16-byte aligned.
+ *   codes  [N, K/2] uint8, 16-byte aligned.  scales [N, K/32] uint16, 2-byte aligned.
+ *   K % 32 == 0 (else UNSUPPORTED_SHAPE).  N == 0 or K == 0: nothing to do, OK.
+ * Bit-exact with the rule above: IEEE fp32 division (no fast-math), fp16
+ * round-to-nearest-even, round half away from zero, clamp to [-8, 7].
+ */
+int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,
+            hipStream_t stream);
+
+/*
+ * q4_gemv_skinny: Y[M, N] = X[M, K] . What^T for 1 <= M <= 8 (decode, verify).
+ *   x      [M, K] fp16, 16-byte aligned.      y [M, N] fp16 (RNE of an fp32
+ *   accumulation), 4-byte aligned.            codes/scales as above.
+ *   split_k: 0 = library choice, else 1..64 slices of K reduced in a fixed
+ *   order (deterministic: the same inputs give bit-identical outputs).
+ *   ws / ws_bytes: device workspace of at least q4_gemv_skinny_ws_bytes(M, N,
+ *   K, split_k) bytes (0 bytes when that function returns 0; ws may then be
+ *   NULL).  The workspace holds fp32 partial sums and per-tile arrival
+ *   counters: it must be zero-filled once before its first use, and every
+ *   call leaves the counters zeroed again for the next call.
+ *   M outside [1, 8] or K % 32 != 0: UNSUPPORTED_SHAPE.  N == 0: OK, nothing
+ *   enqueued.  K == 0: y is filled with zeros.
+ */
+size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
+int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                   uint16_t* y, int M, int64_t N, int64_t K, int split_k,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * a8_quantize_act: per token m and 64-channel group g,
+ *   sa[m, g] = fl32(absmax / 127),
+ *   xq[m, k] = clamp(round_half_away(fl32(x / sa)), -127, 127), 0 if sa == 0.
+ *   x [M, K] fp16 (16-byte aligned), xq [M, K] int8 row-major (16-byte
+ *   aligned), sa [M, K/64] fp32 row-major (4-byte aligned).  K % 64 == 0.
+ *   M == 0 or K == 0: OK, nothing enqueued.
+ */
+int a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* sa,
+                    hipStream_t stream);
+
+/*
+ * a8w4_gemm_prefill: the whole A8 route for any M >= 1:
+ *   quantize x as a8_quantize_act does (into the workspace, in a tiled
+ *   layout private to the library), form the exact int32 block sums
+ *   I[m, n, b] = sum_{k in block b} xq[m, k] * q[n, k] on int8 matrix cores,
+ *   and write y[m, n] = fp16_RNE(sum_b sa[m, b/2] * d[n, b] * I[m, n, b])
+ *   with the rescale in fp32.
+ *   x [M, K] fp16 16-byte aligned; y [M, N] fp16 4-byte aligned.
+ *   K % 64 == 0 and N % 32 == 0 (else UNSUPPORTED_SHAPE).
+ *   ws: at least a8w4_ws_bytes(M, K) bytes, 256-byte aligned.
+ *   M == 0 or N == 0: OK, nothing enqueued.  K == 0: y filled with zeros.
+ */
+size_t a8w4_ws_bytes(int64_t M, int64_t K);
+int a8w4_gemm_prefill(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                      uint16_t* y, int64_t M, int64_t N, int64_t K,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * a8w4_debug_block_acc: test hook.  Same activation quantization and the
+ * same int8 matrix-core kernel as a8w4_gemm_prefill, but the epilogue
+ * writes the exact int32 block sums acc[m, n, b] (row-major [M, N, K/32])
+ * instead of the rescaled result.  Same shape rules and workspace.
+ */
+int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
+                         int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* q4w_status_str(int status);
+
+/* hipError_t of the last call on this thread that returned Q4W_ERR_HIP. */
+int q4w_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4W_H */
