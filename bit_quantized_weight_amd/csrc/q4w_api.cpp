@@ -1,0 +1,138 @@
+// C ABI of libq4w (declared in include/q4w.h): host-side argument checks,
+// workspace sizing and kernel launches.  Every check runs before the first
+// HIP call, so each error status can be produced without a GPU.
+
+#include "q4w.h"
+#include "q4w_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return Q4W_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return Q4W_ERR_HIP;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // kernels index rows and columns with 32-bit ints
+// The skinny kernel addresses one workgroup's rows (<= 64 x K/2 bytes) through
+// a buffer resource with a 32-bit byte range.
+constexpr int64_t kMaxSkinnyK = int64_t(1) << 24;
+
+}  // namespace
+
+extern "C" {
+
+int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,
+            hipStream_t stream) {
+  if (N < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
+  if (K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0 || K == 0) return Q4W_OK;
+  if (!w || !codes || !scales) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return Q4W_ERR_MISALIGNED;
+  return hip_status(q4w::launch_pack(w, N, K, codes, scales, stream));
+}
+
+size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k) {
+  if (M < 1 || M > 8 || N <= 0 || N >= kMaxDim || K <= 0 || K > kMaxSkinnyK ||
+      K % q4w::kBlock != 0 || split_k < 0 || split_k > 64)
+    return 0;
+  return q4w::plan_skinny(M, N, K, split_k).ws_bytes;
+}
+
+int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
+                   int M, int64_t N, int64_t K, int split_k, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (N < 0 || K < 0 || split_k < 0 || split_k > 64) return Q4W_ERR_INVALID_ARG;
+  if (M < 1 || M > 8 || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0) return Q4W_OK;
+  if (!y) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(y, 4)) return Q4W_ERR_MISALIGNED;
+  if (K == 0) return hip_status(q4w::launch_fill_zero_u16(y, int64_t(M) * N, stream));
+  if (!x || !codes || !scales) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return Q4W_ERR_MISALIGNED;
+  const q4w::SkinnyPlan p = q4w::plan_skinny(M, N, K, split_k);
+  if (p.ws_bytes > 0) {
+    if (!ws || ws_bytes < p.ws_bytes) return Q4W_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  }
+  return hip_status(q4w::launch_skinny(x, codes, scales, y, M, N, K, p, ws, stream));
+}
+
+int a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* sa,
+                    hipStream_t stream) {
+  if (M < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
+  if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || K >= kMaxDim) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || K == 0) return Q4W_OK;
+  if (!x || !xq || !sa) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sa, 4)) return Q4W_ERR_MISALIGNED;
+  return hip_status(q4w::launch_act_quant_rowmajor(x, M, K, xq, sa, stream));
+}
+
+size_t a8w4_ws_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % q4w::kActGroup != 0) return 0;
+  return q4w::a8_ws_bytes(M, K);
+}
+
+// Shared checks of the A8 entry points: negative = status to return, 1 = nothing
+// to do, 2 = empty reduction (K == 0), 0 = launch.
+static int a8_common(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                     bool need_scales, void* out, size_t out_align, int64_t M, int64_t N,
+                     int64_t K, void* ws, size_t ws_bytes) {
+  if (M < 0 || N < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
+  if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || N == 0) return 1;  // nothing to do
+  if (!out) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(out, out_align)) return Q4W_ERR_MISALIGNED;
+  if (K == 0) return 2;            // empty reduction
+  if (!x || !codes || (need_scales && !scales)) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || (need_scales && !aligned(scales, 2)))
+    return Q4W_ERR_MISALIGNED;
+  if (!ws || ws_bytes < q4w::a8_ws_bytes(M, K)) return Q4W_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  return Q4W_OK;
+}
+
+int a8w4_gemm_prefill(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
+                      int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  const int c = a8_common(x, codes, scales, true, y, 4, M, N, K, ws, ws_bytes);
+  if (c < 0) return c;
+  if (c == 1) return Q4W_OK;
+  if (c == 2) return hip_status(q4w::launch_fill_zero_u16(y, M * N, stream));
+  hipError_t e = q4w::launch_act_quant_tiled(x, M, K, ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(q4w::launch_a8w4_gemm(ws, codes, scales, y, nullptr, M, N, K, stream));
+}
+
+int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc, int64_t M,
+                         int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int c = a8_common(x, codes, nullptr, false, acc, 4, M, N, K, ws, ws_bytes);
+  if (c < 0) return c;
+  if (c == 1 || c == 2) return Q4W_OK;  // K == 0 has no blocks to write
+  hipError_t e = q4w::launch_act_quant_tiled(x, M, K, ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(q4w::launch_a8w4_gemm(ws, codes, nullptr, nullptr, acc, M, N, K, stream));
+}
+
+const char* q4w_status_str(int status) {
+  switch (status) {
+    case Q4W_OK: return "OK";
+    case Q4W_ERR_INVALID_ARG: return "INVALID_ARG";
+    case Q4W_ERR_UNSUPPORTED_SHAPE: return "UNSUPPORTED_SHAPE";
+    case Q4W_ERR_MISALIGNED: return "MISALIGNED";
+    case Q4W_ERR_WORKSPACE: return "WORKSPACE";
+    case Q4W_ERR_HIP: return "HIP";
+    default: return "UNKNOWN";
+  }
+}
+
+int q4w_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

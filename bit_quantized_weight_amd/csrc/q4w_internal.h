@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (q4w_api.hip) and the kernels.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4w {
+
+// ---- 4-bit block format ---------------------------------------------------
+constexpr int kBlock = 32;        // weights per block along K
+constexpr int kBlockBytes = 16;   // packed codes per block
+constexpr int kActGroup = 64;     // activation channels per int8 scale (A8 route)
+
+hipError_t launch_pack(const float* w, int64_t N, int64_t K, uint8_t* codes,
+                       uint16_t* scales, hipStream_t s);
+
+// ---- skinny (M <= 8) weight-streaming matmul ------------------------------
+struct SkinnyPlan {
+  int rows_per_wg;     // output rows per workgroup
+  int row_tiles;       // ceil(N / rows_per_wg)
+  int splits;          // K slices
+  int blocks_per_split;
+  size_t ws_bytes;     // 0 when splits == 1
+  size_t counter_bytes;
+};
+SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k);
+hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                         uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
+                         void* ws, hipStream_t s);
+
+hipError_t launch_fill_zero_u16(uint16_t* y, int64_t count, hipStream_t s);
+
+// ---- A8 prefill -----------------------------------------------------------
+constexpr int kA8TileM = 32;      // rows per MFMA tile of the private activation layout
+
+int64_t a8_padded_rows(int64_t M);
+size_t a8_ws_bytes(int64_t M, int64_t K);
+hipError_t launch_act_quant_rowmajor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq,
+                                     float* sa, hipStream_t s);
+hipError_t launch_act_quant_tiled(const uint16_t* x, int64_t M, int64_t K, void* ws,
+                                  hipStream_t s);
+hipError_t launch_a8w4_gemm(const void* ws, const uint8_t* codes, const uint16_t* scales,
+                            uint16_t* y, int32_t* acc_debug, int64_t M, int64_t N,
+                            int64_t K, hipStream_t s);
+
+}  // namespace q4w

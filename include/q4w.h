@@ -83,8 +83,8 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
  *   NULL).  The workspace holds fp32 partial sums and per-tile arrival
  *   counters: it must be zero-filled once before its first use, and every
  *   call leaves the counters zeroed again for the next call.
- *   M outside [1, 8] or K % 32 != 0: UNSUPPORTED_SHAPE.  N == 0: OK, nothing
- *   enqueued.  K == 0: y is filled with zeros.
+ *   M outside [1, 8], K % 32 != 0 or K > 2^24: UNSUPPORTED_SHAPE.  N == 0: OK,
+ *   nothing enqueued.  K == 0: y is filled with zeros.
  */
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
 int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
@@ -110,7 +110,7 @@ int a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
  *   and write y[m, n] = fp16_RNE(sum_b sa[m, b/2] * d[n, b] * I[m, n, b])
  *   with the rescale in fp32.
  *   x [M, K] fp16 16-byte aligned; y [M, N] fp16 4-byte aligned.
- *   K % 64 == 0 and N % 32 == 0 (else UNSUPPORTED_SHAPE).
+ *   K % 64 == 0 (else UNSUPPORTED_SHAPE); any M, N >= 1.
  *   ws: at least a8w4_ws_bytes(M, K) bytes, 256-byte aligned.
  *   M == 0 or N == 0: OK, nothing enqueued.  K == 0: y filled with zeros.
  */
@@ -123,7 +123,8 @@ int a8w4_gemm_prefill(const uint16_t* x, const uint8_t* codes, const uint16_t* s
  * a8w4_debug_block_acc: test hook.  Same activation quantization and the
  * same int8 matrix-core kernel as a8w4_gemm_prefill, but the epilogue
  * writes the exact int32 block sums acc[m, n, b] (row-major [M, N, K/32])
- * instead of the rescaled result.  Same shape rules and workspace.
+ * instead of the rescaled result.  Same shape rules and workspace; no
+ * scales are read.  Meant for small shapes (the output is M*N*K/32 ints).
  */
 int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
                          int64_t M, int64_t N, int64_t K,

@@ -1,0 +1,140 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+every argument check returns its status before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_weight_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4w.h")
+
+OK, INVALID, SHAPE, ALIGN, WS = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.lib_path()):
+        pytest.fail("libq4w.so is not built (run __graft_entry__.build())")
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["q4_pack", "q4_gemv_skinny", "q4_gemv_skinny_ws_bytes", "a8_quantize_act",
+              "a8w4_gemm_prefill", "a8w4_ws_bytes", "a8w4_debug_block_acc",
+              "q4w_status_str", "q4w_last_hip_error"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in q4w.h but not exported"
+
+
+def test_status_strings(L):
+    assert L.q4w_status_str(0) == b"OK"
+    assert L.q4w_status_str(-4) == b"WORKSPACE"
+    assert L.q4w_status_str(123) == b"UNKNOWN"
+
+
+# Fake "device" addresses: aligned or not.  Every call below must be rejected
+# (or be a no-op) on the host, so these are never dereferenced.
+A = 1 << 20          # 16- and 256-byte aligned
+U = (1 << 20) + 2    # 2-byte aligned only
+NUL = None
+
+
+def p(v):
+    return ctypes.c_void_p(v)
+
+
+def test_pack_checks(L):
+    assert L.q4_pack(p(A), -1, 64, p(A), p(A), NUL) == INVALID
+    assert L.q4_pack(p(A), 4, 48, p(A), p(A), NUL) == SHAPE
+    assert L.q4_pack(p(A), 0, 64, p(A), p(A), NUL) == OK     # empty: no-op
+    assert L.q4_pack(p(A), 4, 0, p(A), p(A), NUL) == OK
+    assert L.q4_pack(NUL, 4, 64, p(A), p(A), NUL) == INVALID
+    assert L.q4_pack(p(U), 4, 64, p(A), p(A), NUL) == ALIGN
+    assert L.q4_pack(p(A), 4, 64, p(U), p(A), NUL) == ALIGN
+    assert L.q4_pack(p(A), 4, 64, p(A), p(A + 1), NUL) == ALIGN
+
+
+def test_gemv_checks(L):
+    g = L.q4_gemv_skinny
+    assert g(p(A), p(A), p(A), p(A), 0, 64, 64, 0, NUL, 0, NUL) == SHAPE    # M < 1
+    assert g(p(A), p(A), p(A), p(A), 9, 64, 64, 0, NUL, 0, NUL) == SHAPE    # M > 8
+    assert g(p(A), p(A), p(A), p(A), 1, 64, 48, 0, NUL, 0, NUL) == SHAPE    # K % 32
+    assert g(p(A), p(A), p(A), p(A), 1, 64, (1 << 24) + 32, 0, NUL, 0, NUL) == SHAPE
+    assert g(p(A), p(A), p(A), p(A), 1, -1, 64, 0, NUL, 0, NUL) == INVALID
+    assert g(p(A), p(A), p(A), p(A), 1, 64, 64, -1, NUL, 0, NUL) == INVALID  # split_k < 0
+    assert g(p(A), p(A), p(A), p(A), 1, 64, 64, 65, NUL, 0, NUL) == INVALID  # split_k > 64
+    assert g(p(A), p(A), p(A), p(A), 1, 0, 64, 0, NUL, 0, NUL) == OK        # N == 0: no-op
+    assert g(p(A), p(A), p(A), NUL, 1, 64, 64, 0, NUL, 0, NUL) == INVALID   # y null
+    assert g(NUL, p(A), p(A), p(A), 1, 64, 64, 0, NUL, 0, NUL) == INVALID
+    assert g(p(U), p(A), p(A), p(A), 1, 64, 64, 0, NUL, 0, NUL) == ALIGN
+    assert g(p(A), p(U), p(A), p(A), 1, 64, 64, 0, NUL, 0, NUL) == ALIGN
+    assert g(p(A), p(A), p(A), p(A + 2), 1, 64, 64, 0, NUL, 0, NUL) == ALIGN
+    # a shape that needs split-K partials rejects a missing or short workspace
+    ws = L.q4_gemv_skinny_ws_bytes(4, 5120, 17408, 0)
+    assert ws > 0
+    assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, NUL, 0, NUL) == WS
+    assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, p(A), ws - 1, NUL) == WS
+    assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, p(A + 16), ws, NUL) == ALIGN
+
+
+def test_gemv_ws_sizes(L):
+    f = L.q4_gemv_skinny_ws_bytes
+    assert f(0, 64, 64, 0) == 0 and f(9, 64, 64, 0) == 0 and f(1, 64, 48, 0) == 0
+    assert f(1, 512, 256, 1) == 0                  # one slice: no partials
+    # explicit split: S slices x M x N fp32 partials plus the counter region
+    s = f(2, 1000, 1024, 4)
+    assert s >= 4 * 2 * 1000 * 4
+    assert s % 256 == 0 or s > 0
+
+
+def test_act_quant_checks(L):
+    q = L.a8_quantize_act
+    assert q(p(A), -1, 64, p(A), p(A), NUL) == INVALID
+    assert q(p(A), 4, 96, p(A), p(A), NUL) == SHAPE
+    assert q(p(A), 0, 64, p(A), p(A), NUL) == OK
+    assert q(NUL, 4, 64, p(A), p(A), NUL) == INVALID
+    assert q(p(U), 4, 64, p(A), p(A), NUL) == ALIGN
+    assert q(p(A), 4, 64, p(A), p(A + 2), NUL) == ALIGN
+
+
+def test_a8_checks(L):
+    gm = L.a8w4_gemm_prefill
+    ws = L.a8w4_ws_bytes(64, 128)
+    assert ws >= 128 * 128
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, 96, p(A), ws, NUL) == SHAPE      # K % 64
+    assert gm(p(A), p(A), p(A), p(A), -1, 32, 128, p(A), ws, NUL) == INVALID
+    assert gm(p(A), p(A), p(A), p(A), 0, 32, 128, p(A), ws, NUL) == OK          # M == 0
+    assert gm(p(A), p(A), p(A), p(A), 64, 0, 128, p(A), ws, NUL) == OK          # N == 0
+    assert gm(p(A), p(A), p(A), NUL, 64, 32, 128, p(A), ws, NUL) == INVALID
+    assert gm(p(A), p(A), NUL, p(A), 64, 32, 128, p(A), ws, NUL) == INVALID
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, 128, NUL, 0, NUL) == WS
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, 128, p(A), ws - 1, NUL) == WS
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, 128, p(A + 16), ws, NUL) == ALIGN
+    assert gm(p(U), p(A), p(A), p(A), 64, 32, 128, p(A), ws, NUL) == ALIGN
+    dbg = L.a8w4_debug_block_acc
+    assert dbg(p(A), p(A), p(A), 64, 32, 96, p(A), ws, NUL) == SHAPE
+    assert dbg(p(A), p(A), p(A), 64, 32, 128, NUL, 0, NUL) == WS
+    assert dbg(p(A), NUL, p(A), 64, 32, 128, p(A), ws, NUL) == INVALID
+
+
+def test_binding_loads_lazily_and_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises instead of falling back."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

@@ -1,0 +1,118 @@
+"""A8 prefill route on the GPU: int8 codes/scales and int32 block sums bit-exact,
+rescaled fp16 output within the bar of the A8 oracle."""
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, dev, host, torch_cuda
+from oracle import a8, q4
+from bit_quantized_weight_amd import (a8_quantize_act, a8w4_debug_block_acc, a8w4_gemm, pack,
+                                      synthetic)
+from test_oracle_a8 import _special_acts
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed(n, k, seed):
+    torch = torch_cuda()
+    w = synthetic.weights(n, k, seed)
+    codes, scales = pack(dev(w, torch))
+    q, d = q4.quantize(w)
+    return codes, scales, q, d
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (37, 256), (256, 5120), (5, 17408)])
+def test_act_quant_bit_exact(m, k):
+    torch = torch_cuda()
+    x = synthetic.activations(m, k, 100 + m)
+    xq, sa = a8_quantize_act(dev(x, torch))
+    torch.cuda.synchronize()
+    qa, sa_ref = a8.quantize_act(x)
+    assert np.array_equal(host(xq), qa)
+    assert np.array_equal(host(sa).view(np.uint32), sa_ref.view(np.uint32))
+
+
+def test_act_quant_special():
+    torch = torch_cuda()
+    x = _special_acts()
+    xq, sa = a8_quantize_act(dev(x, torch))
+    torch.cuda.synchronize()
+    qa, sa_ref = a8.quantize_act(x)
+    assert np.array_equal(host(xq), qa)
+    assert np.array_equal(host(sa).view(np.uint32), sa_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 32, 64), (31, 48, 256), (33, 130, 128), (128, 128, 512),
+                                   (130, 257, 192), (256, 512, 5120)])
+def test_block_sums_bit_exact(m, n, k):
+    """Exact int32 block sums from the matrix-core kernel's debug epilogue."""
+    torch = torch_cuda()
+    codes, scales, q, d = _packed(n, k, 200 + n)
+    x = synthetic.activations(m, k, 300 + m)
+    acc = a8w4_debug_block_acc(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    qa, _ = a8.quantize_act(x)
+    assert np.array_equal(host(acc), a8.block_sums(qa, q).astype(np.int32))
+
+
+def test_block_sums_extremes():
+    """|I| = 32 * 127 * 8 = 32512 at the extremes of both code ranges."""
+    torch = torch_cuda()
+    w = np.full((32, 64), -8.0, np.float32)
+    w[:, 0] = 7.0                                       # absmax 8 ... codes: 7 at k=0
+    codes, scales = pack(dev(w, torch))
+    q, d = q4.quantize(w)
+    x = np.full((32, 64), -1.0, np.float16)
+    acc = a8w4_debug_block_acc(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    qa, _ = a8.quantize_act(x)
+    assert np.array_equal(host(acc), a8.block_sums(qa, q).astype(np.int32))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 32, 64), (31, 48, 256), (130, 257, 192), (256, 512, 5120),
+                                   (64, 256, 17408)])
+def test_a8_gemm_vs_oracle(m, n, k):
+    torch = torch_cuda()
+    codes, scales, q, d = _packed(n, k, 400 + n)
+    x = synthetic.activations(m, k, 500 + m)
+    y = a8w4_gemm(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    assert_close(host(y), a8.prefill(x, q, d), what=f"A8 M={m} N={n} K={k}")
+
+
+def test_a8_all_ones():
+    torch = torch_cuda()
+    k = 5120
+    codes, scales = pack(torch.ones((64, k), dtype=torch.float32, device="cuda"))
+    y = a8w4_gemm(torch.ones((40, k), dtype=torch.float16, device="cuda"), codes, scales)
+    torch.cuda.synchronize()
+    assert np.all(host(y) == np.float16(5120.0))
+
+
+def test_prefill_full_size_sampled():
+    """The A8 prefill GEMM at M = 2048, K = 5120, N = 17408 (the launch the
+    benchmark times); every column of 24 sampled token rows checked."""
+    torch = torch_cuda()
+    wl = synthetic.WORKLOADS["prefill_a8"]
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    codes, scales, q, d = _packed(N, K, synthetic.WEIGHT_SEED)
+    x = synthetic.activations(M, K, synthetic.ACT_SEED)
+    y = a8w4_gemm(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 127, 128, 1023, M - 1],
+                                     np.random.default_rng(7).integers(0, M, 16)]))
+    yh = host(y)[rows]
+    ref = a8.prefill(x[rows], q, d)
+    assert_close(yh, ref, what="prefill_a8 sampled rows")
+
+
+def test_a8_empty_shapes():
+    torch = torch_cuda()
+    codes, scales, q, d = _packed(32, 128, 600)
+    y = a8w4_gemm(torch.zeros((0, 128), dtype=torch.float16, device="cuda"), codes, scales)
+    assert y.shape == (0, 32)
+    y = a8w4_gemm(torch.zeros((3, 0), dtype=torch.float16, device="cuda"),
+                  torch.zeros((32, 0), dtype=torch.uint8, device="cuda"),
+                  torch.zeros((32, 0), dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (3, 32) and not host(y).any()

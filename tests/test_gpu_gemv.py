@@ -1,0 +1,148 @@
+"""q4_gemv_skinny on the GPU against the fp64 oracle (M = 1..8)."""
+
+import functools
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, dev, host, torch_cuda
+from oracle import q4
+from bit_quantized_weight_amd import gemv, pack, synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=4)
+def packed(n, k, seed):
+    """Weights packed on the GPU plus the oracle's own quantization of them."""
+    torch = torch_cuda()
+    w = synthetic.weights(n, k, seed)
+    codes, scales = pack(dev(w, torch))
+    q, d = q4.quantize(w)
+    return codes, scales, q, d
+
+
+def run(x, codes, scales, split_k=0):
+    torch = torch_cuda()
+    y = gemv(dev(x, torch), codes, scales, split_k=split_k)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def test_tiny_matvec():
+    codes, scales, q, d = packed(512, 256, 0)
+    x = synthetic.activations(1, 256, 1)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what="tiny")
+
+
+@pytest.mark.parametrize("m", range(1, 9))
+@pytest.mark.parametrize("n,k", [(100, 96), (300, 1056), (64, 512), (257, 5120), (70, 8192)])
+def test_shapes_and_ragged_tails(m, n, k):
+    """Ragged N (not a multiple of the 64-row tile) and K (not a multiple of 512)."""
+    codes, scales, q, d = packed(n, k, 10 + n)
+    x = synthetic.activations(m, k, 20 + m)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what=f"M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
+def test_explicit_split_k(split):
+    codes, scales, q, d = packed(200, 2048, 30)
+    x = synthetic.activations(3, 2048, 31)
+    ref = q4.matmul(x, q, d)
+    y1 = run(x, codes, scales, split)
+    assert_close(y1, ref, what=f"split={split}")
+    y2 = run(x, codes, scales, split)
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
+
+
+def test_one_hot_bit_exact():
+    """x = e_k gives fp16(q[n,k] * d[n,k//32]): one product, rounded once."""
+    n, k = 96, 256
+    codes, scales, q, d = packed(n, k, 40)
+    for start in range(0, k, 8):
+        x = np.zeros((8, k), np.float16)
+        for r in range(8):
+            x[r, start + r] = 1.0
+        y = run(x, codes, scales)
+        for r in range(8):
+            kk = start + r
+            want = (q[:, kk].astype(np.float64) * d[:, kk // 32].astype(np.float64)).astype(np.float16)
+            assert np.array_equal(y[r], want), kk
+
+
+@pytest.mark.parametrize("k,y16", [(256, 256.0), (5120, 5120.0), (17408, 17408.0)])
+def test_all_ones_closed_form(k, y16):
+    """W = 1, x = 1: y = K (1 - 2**-12) exactly in fp32, which rounds to K in fp16."""
+    torch = torch_cuda()
+    codes, scales = pack(torch.ones((64, k), dtype=torch.float32, device="cuda"))
+    for m in (1, 5):
+        y = run(np.ones((m, k), np.float16), codes, scales)
+        assert np.all(y == np.float16(y16)), (m, np.unique(y))
+
+
+def test_decode_gate_up():
+    """Decode GEMV, FFN gate/up shape: M = 1, K = 5120, N = 17408."""
+    w = synthetic.WORKLOADS["decode_gate_up"]
+    codes, scales, q, d = packed(w["N"], w["K"], synthetic.WEIGHT_SEED)
+    x = synthetic.activations(1, w["K"], synthetic.ACT_SEED)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what="decode_gate_up")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5])
+def test_verify_down(m):
+    """Speculative verify, down-projection shape: K = 17408, N = 5120, M = 1..5."""
+    w = synthetic.WORKLOADS["verify_down"]
+    codes, scales, q, d = packed(w["N"], w["K"], synthetic.WEIGHT_SEED)
+    x = synthetic.activations(m, w["K"], synthetic.ACT_SEED)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what=f"verify_down M={m}")
+
+
+def test_invariants_bit_exact():
+    """Deterministic reduction: y(2x) = 2 y(x), y(-x) = -y(x), repeats identical."""
+    codes, scales, q, d = packed(5120, 17408, synthetic.WEIGHT_SEED)
+    x = synthetic.activations(4, 17408, 50)
+    y = run(x, codes, scales)
+    y2 = run((x.astype(np.float32) * 2).astype(np.float16), codes, scales)
+    yn = run(-x, codes, scales)
+    assert np.array_equal(y2, (y.astype(np.float32) * 2).astype(np.float16))
+    assert np.array_equal(yn, -y)
+    for _ in range(10):
+        assert np.array_equal(run(x, codes, scales).view(np.uint16), y.view(np.uint16))
+
+
+def test_permuted_rows_permute_outputs():
+    codes, scales, q, d = packed(300, 1056, 60)
+    x = synthetic.activations(2, 1056, 61)
+    y = run(x, codes, scales)
+    perm = np.random.default_rng(0).permutation(300)
+    torch = torch_cuda()
+    idx = torch.from_numpy(perm).cuda()
+    yp = run(x, codes[idx].contiguous(), scales[idx].contiguous())
+    assert np.array_equal(yp.view(np.uint16), y[:, perm].view(np.uint16))
+
+
+def test_tiny_and_large_activations():
+    """fp16 subnormal activations and large magnitudes stay within the bar."""
+    codes, scales, q, d = packed(128, 1024, 70)
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal((3, 1024)) * np.array([[1e-6], [1.0], [300.0]])).astype(np.float16)
+    y = run(x, codes, scales)
+    ref = q4.matmul(x, q, d)
+    for r in range(3):
+        assert_close(y[r:r + 1], ref[r:r + 1], what=f"row {r}")
+
+
+def test_empty_shapes():
+    torch = torch_cuda()
+    codes, scales, q, d = packed(64, 256, 80)
+    # K == 0: empty sum, zeros
+    y = gemv(torch.zeros((2, 0), dtype=torch.float16, device="cuda"),
+             torch.zeros((64, 0), dtype=torch.uint8, device="cuda"),
+             torch.zeros((64, 0), dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (2, 64) and not host(y).any()
+    # N == 0
+    y = gemv(torch.ones((1, 256), dtype=torch.float16, device="cuda"),
+             torch.zeros((0, 128), dtype=torch.uint8, device="cuda"),
+             torch.zeros((0, 8), dtype=torch.float16, device="cuda"))
+    assert y.shape == (1, 0)
