@@ -16,11 +16,13 @@
 //  * Activations are staged once per workgroup into LDS in a permuted fp16
 //    layout matching the in-register unpack below, plus a per-block bias.
 //  * Unpack: (w & 0x000F000F) ^ 0x64086408 flips each nibble's sign bit
-//    (two's complement q -> u = q + 8) and inserts the fp16 exponent, giving
-//    the pair (1024 + u0, 1024 + u4) in one v_bitop3; the 0x00F0 mask gives
-//    (1024 + 16 u) for odd nibbles, whose activations are pre-divided by 16.  v_dot2_f32_f16 then accumulates in fp32
-//    and the constant parts (1032 per even, 72 per odd activation) are
-//    removed exactly by starting each block's accumulator at -bias.  The
+//    (two's complement q -> u = q + 8) and inserts the fp16 exponent of 1024
+//    (mantissa LSB = 1), giving the pair (1024 + u0, 1024 + u4) in one
+//    v_bitop3.  Odd nibbles sit 4 bits higher, so they get the exponent of 64
+//    (mantissa LSB = 1/16): (w & 0x00F000F0) ^ 0x54805480 = (64 + u1, 64 + u5).
+//    v_dot2_f32_f16 accumulates in fp32 against unscaled fp16 activations and
+//    the constant parts (1032 per even, 72 per odd activation) are removed
+//    exactly by starting each block's accumulator at -bias.  The
 //    block scale multiplies the block partial once (fp32 FMA).
 //  * 16-lane DPP rotations reduce each row; K can be split over workgroups
 //    (split-K) whose fp32 partials are summed in a fixed order by the last
@@ -93,10 +95,9 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   uint4* xs = smem;                                          // [M][4][bpad] fp16 quads
   float* cs = reinterpret_cast<float*>(smem + M * 4 * bpad); // [M][bpad] bias
 
-  // ---- stage the activation slice (permuted, odd positions / 16) ----------
-  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  // ---- stage the activation slice in the unpack's pair order --------------
   const uint32_t k1032 = 0x64086408u;   // fp16 pair (1032, 1032)
-  const uint32_t k1152 = 0x64806480u;   // fp16 pair (1152, 1152)
+  const uint32_t k72 = 0x54805480u;     // fp16 pair (72, 72)
   for (int u = tid; u < M * bpad; u += kThreads) {
     const int m = u / bpad;
     const int b = u - m * bpad;
@@ -116,14 +117,14 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
       const uint32_t w0 = raw[q].x, w1 = raw[q].y, w2 = raw[q].z, w3 = raw[q].w;
       uint4 o;
       o.x = (w0 & 0xFFFFu) | (w2 << 16);                               // (e0, e4)
-      o.y = __builtin_bit_cast(uint32_t, as_h2((w0 >> 16) | (w2 & 0xFFFF0000u)) * sixteenth);  // (e1, e5)/16
+      o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);                           // (e1, e5)
       o.z = (w1 & 0xFFFFu) | (w3 << 16);                               // (e2, e6)
-      o.w = __builtin_bit_cast(uint32_t, as_h2((w1 >> 16) | (w3 & 0xFFFF0000u)) * sixteenth);  // (e3, e7)/16
+      o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);                           // (e3, e7)
       xs[(m * 4 + q) * bpad + b] = o;
       c = dot2(o.x, k1032, c);
-      c = dot2(o.y, k1152, c);
+      c = dot2(o.y, k72, c);
       c = dot2(o.z, k1032, c);
-      c = dot2(o.w, k1152, c);
+      c = dot2(o.w, k72, c);
     }
     cs[m * bpad + b] = -c;
   }
@@ -187,14 +188,14 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
       for (int m = 0; m < M; ++m) xq[m] = xs[(m * 4 + q) * bpad + b];
 #pragma unroll
       for (int i = 0; i < RL; ++i) {
-        // (w & mask) ^ (magic | sign bits): flips each nibble's sign bit
-        // (two's complement -> q + 8) and inserts the fp16 exponent 0x64.
+        // (w & mask) ^ (exponent | sign bits): flips each nibble's sign bit
+        // (two's complement -> u = q + 8) and inserts an fp16 exponent.
         const uint32_t w = word(c[i], q);
         const uint32_t w8 = w >> 8;
-        const uint32_t p0 = (w & 0x000F000Fu) ^ 0x64086408u;   // 1024 + u, even nibbles 0, 4
-        const uint32_t p1 = (w & 0x00F000F0u) ^ 0x64806480u;   // 1024 + 16 u, odd nibbles 1, 5
-        const uint32_t p2 = (w8 & 0x000F000Fu) ^ 0x64086408u;  // nibbles 2, 6
-        const uint32_t p3 = (w8 & 0x00F000F0u) ^ 0x64806480u;  // nibbles 3, 7
+        const uint32_t p0 = (w & 0x000F000Fu) ^ 0x64086408u;   // 1024 + u, nibbles 0, 4
+        const uint32_t p1 = (w & 0x00F000F0u) ^ 0x54805480u;   // 64 + u, nibbles 1, 5
+        const uint32_t p2 = (w8 & 0x000F000Fu) ^ 0x64086408u;  // 1024 + u, nibbles 2, 6
+        const uint32_t p3 = (w8 & 0x00F000F0u) ^ 0x54805480u;  // 64 + u, nibbles 3, 7
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           float a = acc[i][m];
@@ -328,7 +329,10 @@ SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   p.blocks_per_split = bps;
   p.splits = (nb + bps - 1) / bps;
   if (p.splits > 1) {
-    p.counter_bytes = (((size_t)p.row_tiles * 4 + 255) / 256) * 256;
+    // Counters live in a fixed region at the start of every workspace and
+    // partials always start after it, so a workspace shared between shapes
+    // never has one shape's partials where another shape's counters are.
+    p.counter_bytes = kCounterRegionBytes;
     p.ws_bytes = p.counter_bytes + (size_t)p.splits * M * N * sizeof(float);
   }
   return p;

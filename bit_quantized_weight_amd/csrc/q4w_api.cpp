@@ -37,7 +37,7 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
 }
 
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k) {
-  if (M < 1 || M > 8 || N <= 0 || N >= kMaxDim || K <= 0 || K > kMaxSkinnyK ||
+  if (M < 1 || M > 8 || N <= 0 || N > q4w::kMaxSkinnyN || K <= 0 || K > kMaxSkinnyK ||
       K % q4w::kBlock != 0 || split_k < 0 || split_k > 64)
     return 0;
   return q4w::plan_skinny(M, N, K, split_k).ws_bytes;
@@ -48,7 +48,7 @@ int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scal
                    hipStream_t stream) {
   if (N < 0 || K < 0 || split_k < 0 || split_k > 64) return Q4W_ERR_INVALID_ARG;
   if (M < 1 || M > 8 || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (N >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N > q4w::kMaxSkinnyN || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (N == 0) return Q4W_OK;
   if (!y) return Q4W_ERR_INVALID_ARG;
   if (!aligned(y, 4)) return Q4W_ERR_MISALIGNED;

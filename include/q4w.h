@@ -80,11 +80,12 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
  *   order (deterministic: the same inputs give bit-identical outputs).
  *   ws / ws_bytes: device workspace of at least q4_gemv_skinny_ws_bytes(M, N,
  *   K, split_k) bytes (0 bytes when that function returns 0; ws may then be
- *   NULL).  The workspace holds fp32 partial sums and per-tile arrival
- *   counters: it must be zero-filled once before its first use, and every
- *   call leaves the counters zeroed again for the next call.
- *   M outside [1, 8], K % 32 != 0 or K > 2^24: UNSUPPORTED_SHAPE.  N == 0: OK,
- *   nothing enqueued.  K == 0: y is filled with zeros.
+ *   NULL).  Layout: a fixed 64 KiB region of per-tile arrival counters, then
+ *   fp32 partial sums.  The workspace must be zero-filled once before its
+ *   first use; every completed call leaves the counter region zeroed again,
+ *   so one workspace may serve any sequence of shapes (not concurrently).
+ *   M outside [1, 8], K % 32 != 0, K > 2^24 or N > 2^20: UNSUPPORTED_SHAPE.
+ *   N == 0: OK, nothing enqueued.  K == 0: y is filled with zeros.
  */
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
 int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,

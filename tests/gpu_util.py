@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: device transfer and the tolerance bar."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -31,5 +33,9 @@ def max_err_rel_rms(y, ref):
 
 def assert_close(y_fp16, ref, tol=TOL_REL_RMS, what=""):
     e = max_err_rel_rms(np.asarray(y_fp16, np.float16).astype(np.float64), ref)
+    log = os.environ.get("Q4W_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(f"{what}\t{e:.3e}\n")
     assert e <= tol, f"{what} max err {e:.3e} x RMS > {tol:.1e}"
     return e
