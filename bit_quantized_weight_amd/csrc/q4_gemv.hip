@@ -9,10 +9,15 @@
 // (page 3, MTP with n_max = 3, i.e. M = 4).
 //
 // gfx950 design (HBM-bound; VALU only):
-//  * A wave is 4 row-slots x 16 lanes.  Lane j of a row-slot owns 32-weight
-//    blocks j, j+16, j+32, ... of its rows, so each dwordx4 load of a wave
-//    reads 4 rows x 256 contiguous bytes of codes: coalesced 128-bit loads.
-//    Every lane carries RL rows, re-using its activation registers RL times.
+//  * A wave is 2 row-slots x 32 lanes.  Lane j of a slot owns 32-weight blocks
+//    j, j+32, j+64, ... of its rows, so one 128-bit load of a wave reads two
+//    rows x 512 contiguous bytes of codes.  Each lane carries RL rows and
+//    re-uses its activation registers RL times.
+//  * Every step of a workgroup's K-slice is requested up front (a register
+//    ring when the slice is longer than the ring): on MI355X a 50 MB stream
+//    only reaches full bandwidth when each wave has all of its bytes in
+//    flight at once.  Lanes past the end of the slice use an out-of-range
+//    buffer offset, which returns zeros without touching memory.
 //  * Activations are staged once per workgroup into LDS in a permuted fp16
 //    layout matching the in-register unpack below, plus a per-block bias.
 //  * Unpack: (w & 0x000F000F) ^ 0x64086408 flips each nibble's sign bit
@@ -22,11 +27,11 @@
 //    (mantissa LSB = 1/16): (w & 0x00F000F0) ^ 0x54805480 = (64 + u1, 64 + u5).
 //    v_dot2_f32_f16 accumulates in fp32 against unscaled fp16 activations and
 //    the constant parts (1032 per even, 72 per odd activation) are removed
-//    exactly by starting each block's accumulator at -bias.  The
-//    block scale multiplies the block partial once (fp32 FMA).
-//  * 16-lane DPP rotations reduce each row; K can be split over workgroups
+//    exactly by starting each block's accumulator at -bias.  The block scale
+//    multiplies the block partial once (fp32 FMA).
+//  * 32-lane DPP/swizzle reduction per row.  K can be split over workgroups
 //    (split-K) whose fp32 partials are summed in a fixed order by the last
-//    workgroup to arrive (one kernel, deterministic).
+//    workgroup to arrive (one kernel, deterministic, no cache flushes).
 
 #include "q4w_internal.h"
 #include <hip/hip_fp16.h>
@@ -36,9 +41,10 @@ namespace {
 
 constexpr int kWaves = 4;               // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLanesPerRow = 16;        // lanes sharing one row along K
+constexpr int kLanesPerRow = 32;        // lanes sharing one row along K
 constexpr int kSlots = 64 / kLanesPerRow;
-constexpr int kLdsBudget = 40 * 1024;   // activation staging bytes per workgroup
+constexpr int kLdsBudget = 48 * 1024;   // activation staging bytes per workgroup
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -52,12 +58,14 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
-__device__ __forceinline__ float row16_sum(float v) {
+// Sum over each 32-lane half of the wave; every lane of the half gets the total.
+__device__ __forceinline__ float half_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+  // lane l and lane l ^ 16 (bitmask swizzle: and 0x1F, xor 0x10)
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
   return v;
 }
 
@@ -65,21 +73,28 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+}  // namespace
+
 // Rows per lane: more rows re-use the activation registers more (less LDS
-// traffic per weight) at the cost of fewer workgroups.
-template <int M> struct RowsPerLane { static constexpr int value = 4; };
+// traffic per weight) at the cost of registers and of fewer workgroups.
+__host__ __device__ constexpr int rows_per_lane(int M) { return M == 1 ? 1 : (M <= 4 || M >= 7) ? 2 : 4; }
+// Steps requested at once per wave (the register ring).
+__host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : M <= 4 ? 4 : 3; }
+// Occupancy target (waves per SIMD).
+__host__ __device__ constexpr int waves_per_simd(int M) { return M <= 3 ? 4 : M == 4 ? 3 : 2; }
 
-// Occupancy target per M: enough waves per SIMD to keep loads in flight.
-template <int M> struct WavesPerEu { static constexpr int value = M <= 2 ? 4 : 3; };
+namespace {
 
-template <int M>
+// kRing = false: every slice fits the ring (steps <= P), one pass, no refills.
+template <int M, bool kRing>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(WavesPerEu<M>::value, 8)))
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(M), 8)))
 skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
               const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
               float* __restrict__ partial, uint32_t* __restrict__ counters,
               int N, int K, int bps, int S) {
-  constexpr int RL = RowsPerLane<M>::value;
+  constexpr int RL = rows_per_lane(M);
+  constexpr int P = ring_steps(M);
   constexpr int kRowsPerWg = kWaves * kSlots * RL;
   extern __shared__ uint4 smem[];
 
@@ -92,8 +107,47 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   const int steps = (nbs + kLanesPerRow - 1) / kLanesPerRow;
   const int bpad = steps * kLanesPerRow;     // slice length padded to whole steps
 
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int slot = lane / kLanesPerRow;
+  const int j = lane % kLanesPerRow;
+  const int tile_row0 = tile * kRowsPerWg;
+  const int rl0 = (wave * kSlots + slot) * RL;   // first row of this lane, tile-local
+
+  // Buffer resources cover this workgroup's rows only; a lane whose row is
+  // past N reads zeros (hardware range check), so rows need no clamping.
+  const int rows_here = min(kRowsPerWg, N - tile_row0);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + (size_t)tile_row0 * nb), 0, rows_here * nb * kBlockBytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + (size_t)tile_row0 * nb), 0, rows_here * nb * 2, kRsrcWord3);
+  uint32_t vblk[RL];   // block index (tile-local) of this lane's block in step 0, per row
+#pragma unroll
+  for (int i = 0; i < RL; ++i) vblk[i] = (uint32_t)((rl0 + i) * nb + kb0 + j);
+
+  // The ring: buf[p] holds step t with t % P == p.  A lane whose block is past
+  // the slice end (including whole steps past the end) gets an out-of-range
+  // offset: the load returns zeros without a memory request.
+  uint4 buf[P][RL];
+  uint32_t sbuf[P][RL];
+  auto load_step = [&](int t, uint4 (&c)[RL], uint32_t (&sc)[RL]) {
+    const bool live = t * kLanesPerRow + j < nbs;
+#pragma unroll
+    for (int i = 0; i < RL; ++i) {
+      const uint32_t vo = live ? vblk[i] * kBlockBytes : kOutOfRange;
+      const uint32_t so = live ? vblk[i] * 2 : kOutOfRange;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kLanesPerRow * kBlockBytes, 0);
+      c[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kLanesPerRow * 2, 0);
+    }
+  };
+  // The weight loads go out before the activations are staged, so their HBM
+  // latency overlaps the staging.
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_step(p, buf[p], sbuf[p]);
+
   uint4* xs = smem;                                          // [M][4][bpad] fp16 quads
-  float* cs = reinterpret_cast<float*>(smem + M * 4 * bpad); // [M][bpad] bias
+  float* cs = reinterpret_cast<float*>(smem + M * 4 * bpad); // [M][bpad] -bias
 
   // ---- stage the activation slice in the unpack's pair order --------------
   const uint32_t k1032 = 0x64086408u;   // fp16 pair (1032, 1032)
@@ -131,47 +185,12 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   __syncthreads();
 
   // ---- stream the weights -----------------------------------------------
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int slot = lane >> 4;
-  const int j = lane & (kLanesPerRow - 1);
-  const int row0 = tile * kRowsPerWg + (wave * kSlots + slot) * RL;
-
-  // Buffer resources cover this workgroup's rows only; a lane whose row is
-  // past N reads zeros (hardware range check), so rows need no clamping.
-  const int tile_row0 = tile * kRowsPerWg;
-  const int rows_here = min(kRowsPerWg, N - tile_row0);
-  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(codes + (size_t)tile_row0 * nb), 0, rows_here * nb * kBlockBytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(scales + (size_t)tile_row0 * nb), 0, rows_here * nb * 2, kRsrcWord3);
-  int voff[RL];   // block index (row-local) of this lane's first block, per row
-#pragma unroll
-  for (int i = 0; i < RL; ++i) voff[i] = (row0 - tile_row0 + i) * nb + kb0 + j;
-
   float yacc[RL][M];
 #pragma unroll
   for (int i = 0; i < RL; ++i)
 #pragma unroll
     for (int m = 0; m < M; ++m) yacc[i][m] = 0.f;
 
-  // Two register buffers alternate between "in flight" and "being consumed",
-  // so the loads of step t+1 overlap the arithmetic of step t without any
-  // register copies.  The step offset is wave-uniform (an SGPR).  A lane
-  // whose block lies past the slice reads a neighbouring block of the same
-  // arrays (or zeros past the end); its LDS activations and bias are zero,
-  // so it contributes exactly 0.
-  uint4 bufA[RL], bufB[RL];
-  uint32_t sA[RL], sB[RL];
-  auto load_step = [&](int t, uint4 (&c)[RL], uint32_t (&sc)[RL]) {
-#pragma unroll
-    for (int i = 0; i < RL; ++i) {
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, voff[i] * kBlockBytes,
-                                                          t * kLanesPerRow * kBlockBytes, 0);
-      c[i] = make_uint4(v[0], v[1], v[2], v[3]);
-      sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff[i] * 2, t * kLanesPerRow * 2, 0);
-    }
-  };
   auto compute_step = [&](int t, const uint4 (&c)[RL], const uint32_t (&sc)[RL]) {
     const int b = t * kLanesPerRow + j;
     float acc[RL][M];
@@ -215,61 +234,67 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
     }
   };
 
-  // Loads are unconditional (a step past the end reads data it ignores): a
-  // conditional load would make the compiler wait for every outstanding load
-  // at the merge point and serialize the pipeline.
-  load_step(0, bufA, sA);
+  if (!kRing) {
+    // the whole slice (steps <= P) is already in flight: no refills
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < steps) compute_step(p, buf[p], sbuf[p]);
+  } else {
+    // Refills are unconditional (past the end they are out-of-range, i.e.
+    // no memory request): a conditional load makes the compiler wait for
+    // every outstanding load at the merge point and serializes the ring.
 #pragma unroll 1
-  for (int t = 0; t < steps; t += 2) {
-    load_step(t + 1, bufB, sB);
-    compute_step(t, bufA, sA);
-    load_step(t + 2, bufA, sA);
-    if (t + 1 < steps) compute_step(t + 1, bufB, sB);
+    for (int t0 = 0; t0 < steps; t0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (t0 + p < steps) compute_step(t0 + p, buf[p], sbuf[p]);
+        load_step(t0 + p + P, buf[p], sbuf[p]);
+      }
+    }
   }
 
-  // ---- reduce the 16 lanes of each row; lane j then stores value j -------
+  // ---- reduce the 32 lanes of each row; lane j then stores value j -------
   constexpr int kVals = RL * M;          // (row i, token m) pairs, index i * M + m
-  float tot[RL][M];
+  static_assert(kVals <= kLanesPerRow, "one store pass");
+  float v = 0.f;
 #pragma unroll
   for (int i = 0; i < RL; ++i)
 #pragma unroll
-    for (int m = 0; m < M; ++m) tot[i][m] = row16_sum(yacc[i][m]);
-#pragma unroll
-  for (int pass = 0; pass < (kVals + kLanesPerRow - 1) / kLanesPerRow; ++pass) {
-    const int idx = pass * kLanesPerRow + j;
-    float v = 0.f;
-#pragma unroll
-    for (int i = 0; i < RL; ++i)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        if (idx == i * M + m) v = tot[i][m];
-    if (idx < kVals) {
-      const int i = idx / M;
-      const int m = idx - i * M;
-      const int n = row0 + i;
-      if (n < N) {
-        if (S == 1) y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(v));
-        else partial[((size_t)split * M + m) * N + n] = v;
-      }
+    for (int m = 0; m < M; ++m) {
+      const float s = half_sum(yacc[i][m]);
+      if (j == i * M + m) v = s;
+    }
+  if (j < kVals) {
+    const int i = j / M;
+    const int m = j - i * M;
+    const int n = tile_row0 + rl0 + i;
+    if (n < N) {
+      if (S == 1) y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(v));
+      else  // agent-coherent store: visible to every XCD once complete
+        __hip_atomic_store(&partial[((size_t)split * M + m) * N + n], v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
   if (S == 1) return;
 
   // ---- split-K: the last workgroup of this row tile sums the partials ----
+  // Partials are written and read with agent-scope (cache-coherent) accesses,
+  // so no L2 write-back or invalidate is needed: waiting for this
+  // workgroup's stores to complete before the arrival count is enough.
   __shared__ int is_last;
-  __threadfence();                       // release this thread's partial stores
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned prev = atomicAdd(&counters[tile], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     is_last = (prev == (unsigned)(S - 1));
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();                       // acquire the other workgroups' partials
   for (int o = tid; o < kRowsPerWg * M; o += kThreads) {
     const int m = o / kRowsPerWg;
-    const int n = tile * kRowsPerWg + (o - m * kRowsPerWg);
+    const int n = tile_row0 + (o - m * kRowsPerWg);
     if (n < N) {
       float s = 0.f;
       for (int sp2 = 0; sp2 < S; ++sp2)
@@ -278,7 +303,8 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
       y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(s));
     }
   }
-  if (tid == 0) counters[tile] = 0u;    // leave the workspace ready for the next call
+  if (tid == 0)   // leave the workspace ready for the next call
+    __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void fill_zero_kernel(uint16_t* y, int64_t count) {
@@ -297,34 +323,46 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
     counters = reinterpret_cast<uint32_t*>(ws);
     partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes);
   }
-  hipLaunchKernelGGL(skinny_kernel<M>, dim3(p.row_tiles, p.splits), dim3(kThreads), lds, s, x,
-                     reinterpret_cast<const uint4*>(codes), scales, y, partial, counters, (int)N,
-                     (int)K, p.blocks_per_split, p.splits);
+  const bool ring = bpad / kLanesPerRow > ring_steps(M);
+  if (ring)
+    hipLaunchKernelGGL((skinny_kernel<M, true>), dim3(p.row_tiles, p.splits), dim3(kThreads), lds,
+                       s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
+                       (int)N, (int)K, p.blocks_per_split, p.splits);
+  else
+    hipLaunchKernelGGL((skinny_kernel<M, false>), dim3(p.row_tiles, p.splits), dim3(kThreads), lds,
+                       s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
+                       (int)N, (int)K, p.blocks_per_split, p.splits);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Split plan.  A slice is a whole number of 32-block steps; the number of
+// slices S is chosen so that (a) a slice's activations fit the LDS budget,
+// (b) a slice is at most two rings long, and (c) there are enough
+// workgroups to fill the GPU.  split_k > 0 asks for that many slices (raised
+// when the LDS budget needs more).
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   SkinnyPlan p{};
-  const int rl = 4;  // RowsPerLane<M>::value for every M
-  p.rows_per_wg = kWaves * kSlots * rl;
+  p.rows_per_wg = kWaves * kSlots * rows_per_lane(M);
   p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
   const int nb = (int)(K / kBlock);
-  // largest slice whose staged activations fit the LDS budget, in whole steps
-  int bps_max = kLdsBudget / (M * (4 * 16 + 4));
-  bps_max = (bps_max / kLanesPerRow) * kLanesPerRow;
-  int S = split_k > 0 ? split_k : 1;
-  if (split_k == 0) {
-    const int target_wgs = 512;  // >= 2 workgroups (8 waves) per CU on 256 CUs
-    const int want = (target_wgs + p.row_tiles - 1) / p.row_tiles;
-    const int cap = nb / kLanesPerRow > 0 ? nb / kLanesPerRow : 1;  // >= one step per slice
-    S = want < cap ? want : cap;
-    if (S < 1) S = 1;
+  const int lds_blocks = kLdsBudget / (M * (4 * 16 + 4));      // blocks of one slice in LDS
+  int bps;
+  if (split_k > 0) {
+    bps = (nb + split_k - 1) / split_k;
+    const int cap = (lds_blocks / kLanesPerRow) * kLanesPerRow;
+    if (bps > cap) bps = cap;
+  } else {
+    const int steps_total = (nb + kLanesPerRow - 1) / kLanesPerRow;
+    int max_steps = lds_blocks / kLanesPerRow;
+    if (max_steps > 2 * ring_steps(M)) max_steps = 2 * ring_steps(M);
+    if (max_steps < 1) max_steps = 1;
+    int S = (steps_total + max_steps - 1) / max_steps;
+    const int target_wgs = 1024;   // about four workgroups per CU on 256 CUs
+    while ((int64_t)S * p.row_tiles < target_wgs && steps_total / (S + 1) >= 2) ++S;
+    bps = ((steps_total + S - 1) / S) * kLanesPerRow;
   }
-  int bps = (nb + S - 1) / S;
-  if (split_k == 0) bps = ((bps + kLanesPerRow - 1) / kLanesPerRow) * kLanesPerRow;
-  if (bps > bps_max) bps = bps_max;
   if (bps < 1) bps = 1;
   p.blocks_per_split = bps;
   p.splits = (nb + bps - 1) / bps;

@@ -17,10 +17,10 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, uint8_t* codes,
                        uint16_t* scales, hipStream_t s);
 
 // ---- skinny (M <= 8) weight-streaming matmul ------------------------------
-// Split-K arrival counters: one uint32 per 64-row tile, in a fixed region at
-// the start of the workspace (bounds N to 16384 tiles = 1,048,576 rows).
+// Split-K arrival counters: one uint32 per row tile (32 or 64 rows), in a
+// fixed region at the start of the workspace (16384 tiles: N <= 524,288).
 constexpr size_t kCounterRegionBytes = 64 * 1024;
-constexpr int64_t kMaxSkinnyN = int64_t(kCounterRegionBytes / 4) * 64;
+constexpr int64_t kMaxSkinnyN = int64_t(kCounterRegionBytes / 4) * 32;
 struct SkinnyPlan {
   int rows_per_wg;     // output rows per workgroup
   int row_tiles;       // ceil(N / rows_per_wg)

@@ -84,7 +84,7 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
  *   fp32 partial sums.  The workspace must be zero-filled once before its
  *   first use; every completed call leaves the counter region zeroed again,
  *   so one workspace may serve any sequence of shapes (not concurrently).
- *   M outside [1, 8], K % 32 != 0, K > 2^24 or N > 2^20: UNSUPPORTED_SHAPE.
+ *   M outside [1, 8], K % 32 != 0, K > 2^24 or N > 2^19: UNSUPPORTED_SHAPE.
  *   N == 0: OK, nothing enqueued.  K == 0: y is filled with zeros.
  */
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
