@@ -154,25 +154,56 @@ __global__ void __launch_bounds__(64) act_quant_tiled_kernel(const uint16_t* __r
 }
 
 // ---- int8 MFMA GEMM --------------------------------------------------------
+// MFMA and VALU instructions do not overlap on gfx950 (measured), so the
+// kernel minimizes VALU work per MFMA: the nibble -> int8 unpack and the
+// weight-scale preparation are done once per workgroup into LDS, and the
+// per-output rescale is the three-FMA magic-number form (1.5 FMAs per output
+// element and 32-wide block).  Every operand a wave needs is staged in LDS one
+// chunk ahead (double buffer), so a wave only waits on LDS, and two
+// workgroups fit on a CU.
 constexpr int kTM = 128;          // workgroup tile rows (tokens)
 constexpr int kTN = 128;          // workgroup tile columns (output features)
-constexpr int kChunkBlocks = 8;   // weight blocks staged per LDS chunk (256 K)
+constexpr int kChunkBlocks = 4;   // weight blocks per LDS chunk (128 K)
+constexpr int kChunkGroups = kChunkBlocks / 2;
+constexpr int kMSub = kTM / 32;   // 32-row MFMA subtiles per workgroup
+constexpr int kNSub = kTN / 32;   // 32-column MFMA subtiles per workgroup
 constexpr float kMagic = 12582912.0f;   // 0x4B400000 = 1.5 * 2^23
+constexpr int kSdStride = kTN + 16;       // padding spreads the staging writes over all banks
 
 __device__ __forceinline__ uint32_t lo_codes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_codes(uint32_t w) { return w & 0xF0F0F0F0u; }
 
+// One LDS chunk buffer (36 KB).
+//   bq: int8 B operands (16 x the codes), [n-subtile][block][slot], 16 B per
+//       slot; the operand of MFMA lane l for block b sits in slot l ^ 4b, so
+//       the staging writes (4 rows x 4 blocks per 16 lanes) and the operand
+//       reads (16 consecutive lanes) both touch 16 distinct bank groups.
+//   aq: int8 A operands, [m-subtile][block][lane] (copied from the tiled
+//       activation layout).
+//   sd: d[n, b] / 16 (fp32), [block][column + pad].
+//   sb: -1.5 * 2^23 * (d[n, 2g] + d[n, 2g+1]) / 16, [group][column].
+//   sa: activation scales, [group][row].
+struct ChunkLds {
+  uint4 bq[kNSub * kChunkBlocks * 64];
+  uint4 aq[kMSub * kChunkBlocks * 64];
+  float sd[kChunkBlocks * kSdStride];
+  float sb[kChunkGroups * kTN];
+  float sa[kChunkGroups * kTM];
+};
+
 template <bool kDebug>
 __global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
                  const uint4* __restrict__ codes, const uint16_t* __restrict__ scales,
                  uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg, int M, int N, int K,
                  int mtiles, int ntiles) {
-  __shared__ uint4 lds_b[kTN * kChunkBlocks];        // codes, 16 B per (row, block), swizzled
-  __shared__ uint4 lds_s[kTN];                       // 8 fp16 scales per row
+  __shared__ ChunkLds lds[2];
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
   const int nb = K / kBlock;
   const int G = K / kActGroup;
+  const int nchunks = (nb + kChunkBlocks - 1) / kChunkBlocks;
   const int tid = threadIdx.x;
 
   // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
@@ -191,7 +222,91 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   const int j = lane & 31;
   const int h = lane >> 5;
   const int n_base = nt * kTN;
-  const int mtile32[2] = {(mt * kTM + wm * 64) / kA8TileM, (mt * kTM + wm * 64) / kA8TileM + 1};
+  const int mt32 = mt * kMSub;       // first 32-row activation tile of the workgroup
+
+  // ---- buffer resources (out-of-range offsets read zeros, no traffic) ----
+  const int rows_here = min(kTN, N - n_base);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + (size_t)n_base * nb), 0, rows_here * nb * kBlockBytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(xq_t + (size_t)mt32 * nb * 64), 0, kMSub * nb * 64 * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sa_t + (size_t)mt32 * G * 32), 0, kMSub * G * 32 * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + (size_t)n_base * nb), 0, rows_here * nb * 2, 0x00020000);
+
+  // ---- cooperative chunk staging --------------------------------------------
+  // per thread: 2 weight units (row, block), 4 activation units, 2 scales, 1 sa
+  uint4 rawb[2], rawa[4];
+  uint32_t rawd[2];
+  float rawsa;
+  auto stage_issue = [&](int c) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = it * 256 + tid;          // 128 rows x 4 blocks
+      const int r = u >> 2, bl = u & 3;
+      const int b = c * kChunkBlocks + bl;
+      const uint32_t off = (b < nb) ? (uint32_t)((r * nb + b) * kBlockBytes) : 0x80000000u;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+      rawb[it] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = it * 256 + tid;          // 4 m-subtiles x 4 blocks x 64 lanes
+      const int ms = u >> 8, bl = (u >> 6) & 3, l = u & 63;
+      const int b = c * kChunkBlocks + bl;
+      const uint32_t off = (b < nb) ? (uint32_t)(((ms * nb + b) * 64 + l) * 16) : 0x80000000u;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      rawa[it] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    if (!kDebug) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int u = it * 256 + tid;        // 128 columns x 4 blocks
+        const int r = u >> 2, bl = u & 3;
+        const int b = c * kChunkBlocks + bl;
+        const uint32_t off = (b < nb) ? (uint32_t)((r * nb + b) * 2) : 0x80000000u;
+        rawd[it] = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
+      }
+      {
+        const int gi = tid >> 7, r = tid & 127;  // 2 groups x 128 rows
+        const int g = c * kChunkGroups + gi;
+        const int ms = r >> 5, rr = r & 31;
+        const uint32_t off = (g < G) ? (uint32_t)(((ms * G + g) * 32 + rr) * 4) : 0x80000000u;
+        rawsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
+      }
+    }
+  };
+  auto stage_commit = [&](ChunkLds& L) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int u = it * 256 + tid;
+      const int r = u >> 2, bl = u & 3;
+      const int ns = r >> 5, jj = r & 31;
+      const uint4 w = rawb[it];
+      // K-half 0 of the block is code words 0-1, half 1 is words 2-3
+      L.bq[(ns * kChunkBlocks + bl) * 64 + (jj ^ (4 * bl))] =
+          make_uint4(lo_codes(w.x), hi_codes(w.x), lo_codes(w.y), hi_codes(w.y));
+      L.bq[(ns * kChunkBlocks + bl) * 64 + ((jj + 32) ^ (4 * bl))] =
+          make_uint4(lo_codes(w.z), hi_codes(w.z), lo_codes(w.w), hi_codes(w.w));
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) L.aq[it * 256 + tid] = rawa[it];
+    if (!kDebug) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int u = it * 256 + tid;
+        const int r = u >> 2, bl = u & 3;
+        // the B operand carries 16 q: fold the 1/16 into the scale (exact)
+        const float d = __half2float(__ushort_as_half((unsigned short)rawd[it])) * 0.0625f;
+        L.sd[bl * kSdStride + r] = d;
+        // blocks 2i and 2i+1 of a group sit in adjacent lanes
+        const float dn = __shfl_xor(d, 1, 64);
+        if ((bl & 1) == 0) L.sb[(bl >> 1) * kTN + r] = -kMagic * (d + dn);
+      }
+      L.sa[tid] = rawsa;
+    }
+  };
 
   v16i magic;
 #pragma unroll
@@ -205,94 +320,80 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  for (int kc = 0; kc < nb; kc += kChunkBlocks) {
-    const int nblk = min(kChunkBlocks, nb - kc);
-    __syncthreads();
-    // cooperative stage of codes: kTN rows x 8 blocks, unit u of row r at u ^ (r & 7)
-#pragma unroll
-    for (int it = 0; it < (kTN * kChunkBlocks) / 256; ++it) {
-      const int idx = it * 256 + tid;
-      const int row = idx >> 3;
-      const int u = idx & 7;
-      const int n = min(n_base + row, N - 1);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (u < nblk) v = codes[(size_t)n * nb + kc + u];
-      lds_b[row * kChunkBlocks + (u ^ (row & 7))] = v;
-    }
-    if (!kDebug && tid < kTN) {
-      const int n = min(n_base + tid, N - 1);
-      uint32_t sv[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int u = 0; u < kChunkBlocks; ++u)
-        if (u < nblk) sv[u >> 1] |= (uint32_t)scales[(size_t)n * nb + kc + u] << (16 * (u & 1));
-      lds_s[tid] = make_uint4(sv[0], sv[1], sv[2], sv[3]);
-    }
-    __syncthreads();
+  stage_issue(0);
+  stage_commit(lds[0]);
+  __syncthreads();
 
-    for (int g2 = 0; g2 < nblk; g2 += 2) {
-      const int b0 = kc + g2;
-      const int g = b0 >> 1;
-      // activation operands (two 32-row tiles x two blocks) and scales
-      v4i av[2][2];
-      float sav[2][16];
+#pragma unroll 1
+  for (int c = 0; c < nchunks; ++c) {
+    const ChunkLds& L = lds[c & 1];
+    stage_issue(c + 1);                       // out of range past the last chunk
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-          const uint4 t = xq_t[((size_t)mtile32[mi] * nb + b0 + bi) * 64 + lane];
-          av[mi][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
-        }
-        const float4* sp = reinterpret_cast<const float4*>(sa_t + ((size_t)mtile32[mi] * G + g) * 32);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 f = sp[2 * r + h];
-          sav[mi][4 * r + 0] = f.x; sav[mi][4 * r + 1] = f.y;
-          sav[mi][4 * r + 2] = f.z; sav[mi][4 * r + 3] = f.w;
-        }
-      }
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int row = wn * 64 + ni * 32 + j;
-        // lane (j, h) reads the whole 16 B of block b0 + h, then the two halves
-        // of the wave swap so lane (j, h) holds K-half h of block b0 and of b0+1
-        const uint4 raw = lds_b[row * kChunkBlocks + ((g2 + h) ^ (row & 7))];
-        const auto s02 = __builtin_amdgcn_permlane32_swap(raw.x, raw.z, false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(raw.y, raw.w, false, false);
-        const uint32_t p0 = s02[0], p1 = s13[0];   // block b0, half h
-        const uint32_t q0 = s02[1], q1 = s13[1];   // block b0 + 1, half h
-        const v4i bv0 = v4i{(int)lo_codes(p0), (int)hi_codes(p0), (int)lo_codes(p1), (int)hi_codes(p1)};
-        const v4i bv1 = v4i{(int)lo_codes(q0), (int)hi_codes(q0), (int)lo_codes(q1), (int)hi_codes(q1)};
-        const uint4 sc = lds_s[row];
-        const uint32_t sw = (g2 >> 1) == 0 ? sc.x : (g2 >> 1) == 1 ? sc.y : (g2 >> 1) == 2 ? sc.z : sc.w;
-        // the B operand carries 16 * q, fold the 1/16 into the scales (exact)
-        const float d0 = __half2float(__ushort_as_half((unsigned short)(sw & 0xFFFFu))) * 0.0625f;
-        const float d1 = __half2float(__ushort_as_half((unsigned short)(sw >> 16))) * 0.0625f;
-        const float nc = -kMagic * (d0 + d1);
+    for (int gi = 0; gi < kChunkGroups; ++gi) {
+      const int g = c * kChunkGroups + gi;
+      if (g < G) {   // also keeps the scheduler from interleaving groups (registers)
+        const int bl0 = 2 * gi;
+        v4i av[2][2];
+        float sav[2][16];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-          const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][0], bv0, magic, 0, 0, 0);
-          const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][1], bv1, magic, 0, 0, 0);
-          if (kDebug) {
+          const int ms = wm * 2 + mi;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int mrow = mtile32[mi] * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
-              const int ncol = n_base + wn * 64 + ni * 32 + j;
-              if (mrow < M && ncol < N) {
-                int32_t* o = acc_dbg + ((size_t)mrow * N + ncol) * nb + b0;
-                o[0] = (D0[v] - 0x4B400000) >> 4;
-                o[1] = (D1[v] - 0x4B400000) >> 4;
-              }
+          for (int bi = 0; bi < 2; ++bi) {
+            const uint4 t = L.aq[(ms * kChunkBlocks + bl0 + bi) * 64 + lane];
+            av[mi][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+          }
+          if (!kDebug) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float4 f = *reinterpret_cast<const float4*>(&L.sa[gi * kTM + ms * 32 + 8 * r + 4 * h]);
+              sav[mi][4 * r + 0] = f.x; sav[mi][4 * r + 1] = f.y;
+              sav[mi][4 * r + 2] = f.z; sav[mi][4 * r + 3] = f.w;
             }
-          } else {
+          }
+        }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float s = fmaf(__int_as_float(D0[v]), d0, fmaf(__int_as_float(D1[v]), d1, nc));
-              acc[mi][ni][v] = fmaf(s, sav[mi][v], acc[mi][ni][v]);
+        for (int ni = 0; ni < 2; ++ni) {
+          const int ns = wn * 2 + ni;
+          const int col = ns * 32 + j;
+          const uint4 b0r = L.bq[(ns * kChunkBlocks + bl0) * 64 + (lane ^ (4 * bl0))];
+          const uint4 b1r = L.bq[(ns * kChunkBlocks + bl0 + 1) * 64 + (lane ^ (4 * (bl0 + 1)))];
+          const v4i bv0 = v4i{(int)b0r.x, (int)b0r.y, (int)b0r.z, (int)b0r.w};
+          const v4i bv1 = v4i{(int)b1r.x, (int)b1r.y, (int)b1r.z, (int)b1r.w};
+          float d0 = 0.f, d1 = 0.f, nc = 0.f;
+          if (!kDebug) {
+            d0 = L.sd[bl0 * kSdStride + col];
+            d1 = L.sd[(bl0 + 1) * kSdStride + col];
+            nc = L.sb[gi * kTN + col];
+          }
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) {
+            const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][0], bv0, magic, 0, 0, 0);
+            const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][1], bv1, magic, 0, 0, 0);
+            if (kDebug) {
+              const int ncol = n_base + col;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int mrow = (mt32 + wm * 2 + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (mrow < M && ncol < N) {
+                  int32_t* o = acc_dbg + ((size_t)mrow * N + ncol) * nb + 2 * g;
+                  o[0] = (D0[v] - 0x4B400000) >> 4;
+                  o[1] = (D1[v] - 0x4B400000) >> 4;
+                }
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const float s = fmaf(__int_as_float(D0[v]), d0, fmaf(__int_as_float(D1[v]), d1, nc));
+                acc[mi][ni][v] = fmaf(s, sav[mi][v], acc[mi][ni][v]);
+              }
             }
           }
         }
       }
     }
+    stage_commit(lds[(c + 1) & 1]);            // zeros past the last chunk
+    __syncthreads();
   }
 
   if (kDebug) return;
@@ -300,10 +401,10 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-      const int ncol = n_base + wn * 64 + ni * 32 + j;
+      const int ncol = n_base + (wn * 2 + ni) * 32 + j;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int mrow = mtile32[mi] * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int mrow = (mt32 + wm * 2 + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
         if (mrow < M && ncol < N)
           y[(size_t)mrow * N + ncol] = __half_as_ushort(__float2half_rn(acc[mi][ni][v]));
       }

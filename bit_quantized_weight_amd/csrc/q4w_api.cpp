@@ -86,7 +86,7 @@ static int a8_common(const uint16_t* x, const uint8_t* codes, const uint16_t* sc
                      int64_t K, void* ws, size_t ws_bytes) {
   if (M < 0 || N < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
   if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (M == 0 || N == 0) return 1;  // nothing to do
   if (!out) return Q4W_ERR_INVALID_ARG;
   if (!aligned(out, out_align)) return Q4W_ERR_MISALIGNED;
