@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     a8_quantize_act,
     a8w4_debug_block_acc,
     a8w4_gemm,
+    a8w4_gemm_prepared,
+    a8w4_prepare,
     a8w4_ws_bytes,
     gemv,
     gemv_ws_bytes,

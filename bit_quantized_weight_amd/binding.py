@@ -57,6 +57,10 @@ def lib():
     L.a8w4_ws_bytes.restype = sz
     L.a8w4_gemm_prefill.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     L.a8w4_gemm_prefill.restype = i32
+    L.a8w4_prepare_act.argtypes = [vp, i64, i64, vp, sz, vp]
+    L.a8w4_prepare_act.restype = i32
+    L.a8w4_gemm_prepared.argtypes = [vp, vp, vp, vp, i64, i64, i64, sz, vp]
+    L.a8w4_gemm_prepared.restype = i32
     L.a8w4_debug_block_acc.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
     L.a8w4_debug_block_acc.restype = i32
     L.q4w_status_str.argtypes = [i32]
@@ -167,6 +171,29 @@ def a8w4_gemm(x, codes, scales, y=None):
     ws = _workspace(nb, x.device, "a8")
     _check("a8w4_gemm_prefill", lib().a8w4_gemm_prefill(
         _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, _ptr(ws), nb, _stream()))
+    return y
+
+
+def a8w4_prepare(x, ws=None):
+    """Quantize fp16 X [M, K] once into a workspace (returned) for a8w4_gemm_prepared."""
+    import torch
+    _need(x, torch.float16, "x")
+    m, k = x.shape
+    nb = a8w4_ws_bytes(m, k)
+    if ws is None:
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    _check("a8w4_prepare_act", lib().a8w4_prepare_act(_ptr(x), m, k, _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def a8w4_gemm_prepared(ws, m, k, codes, scales, y=None):
+    """A8 GEMM from a workspace filled by a8w4_prepare -> fp16 Y [M, N]."""
+    import torch
+    n = codes.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float16, device=codes.device)
+    _check("a8w4_gemm_prepared", lib().a8w4_gemm_prepared(
+        _ptr(ws), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, ws.numel(), _stream()))
     return y
 
 

@@ -111,6 +111,31 @@ int a8w4_gemm_prefill(const uint16_t* x, const uint8_t* codes, const uint16_t* s
   return hip_status(q4w::launch_a8w4_gemm(ws, codes, scales, y, nullptr, M, N, K, stream));
 }
 
+int a8w4_prepare_act(const uint16_t* x, int64_t M, int64_t K, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (M < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
+  if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M == 0 || K == 0) return Q4W_OK;
+  if (!x) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return Q4W_ERR_MISALIGNED;
+  if (!ws || ws_bytes < q4w::a8_ws_bytes(M, K)) return Q4W_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  return hip_status(q4w::launch_act_quant_tiled(x, M, K, ws, stream));
+}
+
+int a8w4_gemm_prepared(const void* ws, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
+                       int64_t M, int64_t N, int64_t K, size_t ws_bytes, hipStream_t stream) {
+  // the activations were checked by a8w4_prepare_act; pass a stand-in aligned pointer
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(ws);
+  const int c = a8_common(xs ? xs : nullptr, codes, scales, true, y, 4, M, N, K,
+                          const_cast<void*>(ws), ws_bytes);
+  if (c < 0) return c;
+  if (c == 1) return Q4W_OK;
+  if (c == 2) return hip_status(q4w::launch_fill_zero_u16(y, M * N, stream));
+  return hip_status(q4w::launch_a8w4_gemm(ws, codes, scales, y, nullptr, M, N, K, stream));
+}
+
 int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc, int64_t M,
                          int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int c = a8_common(x, codes, nullptr, false, acc, 4, M, N, K, ws, ws_bytes);

@@ -121,6 +121,23 @@ int a8w4_gemm_prefill(const uint16_t* x, const uint8_t* codes, const uint16_t* s
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The A8 route in two calls, for callers that feed one activation matrix to
+ * several weight matrices (e.g. the gate and up projections share their
+ * input): a8w4_prepare_act quantizes x once into the workspace (the private
+ * tiled layout a8w4_gemm_prefill uses internally), and a8w4_gemm_prepared
+ * runs the int8 matrix-core GEMM from it.  Together they compute exactly what
+ * a8w4_gemm_prefill computes.  Same shape rules, alignments and workspace
+ * size (a8w4_ws_bytes(M, K)); the workspace must not be modified between the
+ * two calls.  M == 0 or K == 0: prepare enqueues nothing; gemm_prepared with
+ * K == 0 fills y with zeros.
+ */
+int a8w4_prepare_act(const uint16_t* x, int64_t M, int64_t K, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+int a8w4_gemm_prepared(const void* ws, const uint8_t* codes, const uint16_t* scales,
+                       uint16_t* y, int64_t M, int64_t N, int64_t K, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
  * a8w4_debug_block_acc: test hook.  Same activation quantization and the
  * same int8 matrix-core kernel as a8w4_gemm_prefill, but the epilogue
  * writes the exact int32 block sums acc[m, n, b] (row-major [M, N, K/32])

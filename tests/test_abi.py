@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["q4_pack", "q4_gemv_skinny", "q4_gemv_skinny_ws_bytes", "a8_quantize_act",
               "a8w4_gemm_prefill", "a8w4_ws_bytes", "a8w4_debug_block_acc",
+              "a8w4_prepare_act", "a8w4_gemm_prepared",
               "q4w_status_str", "q4w_last_hip_error"]:
         assert n in names, n
 
@@ -126,6 +127,17 @@ def test_a8_checks(L):
     assert gm(p(A), p(A), p(A), p(A), 64, 32, 128, p(A), ws - 1, NUL) == WS
     assert gm(p(A), p(A), p(A), p(A), 64, 32, 128, p(A + 16), ws, NUL) == ALIGN
     assert gm(p(U), p(A), p(A), p(A), 64, 32, 128, p(A), ws, NUL) == ALIGN
+    pr = L.a8w4_prepare_act
+    assert pr(p(A), 64, 96, p(A), ws, NUL) == SHAPE
+    assert pr(p(A), 0, 128, p(A), ws, NUL) == OK
+    assert pr(NUL, 64, 128, p(A), ws, NUL) == INVALID
+    assert pr(p(A), 64, 128, p(A), ws - 1, NUL) == WS
+    assert pr(p(U), 64, 128, p(A), ws, NUL) == ALIGN
+    gp = L.a8w4_gemm_prepared
+    assert gp(p(A), p(A), p(A), p(A), 64, 32, 96, ws, NUL) == SHAPE
+    assert gp(p(A), p(A), p(A), p(A), 64, 32, 128, ws - 1, NUL) == WS
+    assert gp(NUL, p(A), p(A), p(A), 64, 32, 128, ws, NUL) == INVALID
+    assert gp(p(A), p(A), NUL, p(A), 64, 32, 128, ws, NUL) == INVALID
     dbg = L.a8w4_debug_block_acc
     assert dbg(p(A), p(A), p(A), 64, 32, 96, p(A), ws, NUL) == SHAPE
     assert dbg(p(A), p(A), p(A), 64, 32, 128, NUL, 0, NUL) == WS

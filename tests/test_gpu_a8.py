@@ -80,6 +80,24 @@ def test_a8_gemm_vs_oracle(m, n, k):
     assert_close(host(y), a8.prefill(x, q, d), what=f"A8 M={m} N={n} K={k}")
 
 
+def test_prepare_then_gemm_matches_one_call():
+    """Quantize once, reuse for two weight matrices; bit-identical to the one-call route."""
+    torch = torch_cuda()
+    from bit_quantized_weight_amd import a8w4_gemm_prepared, a8w4_prepare
+    k = 1024
+    c1, s1, q1, d1 = _packed(96, k, 700)
+    c2, s2, q2, d2 = _packed(160, k, 701)
+    x = dev(synthetic.activations(70, k, 702), torch)
+    ws = a8w4_prepare(x)
+    y1 = a8w4_gemm_prepared(ws, 70, k, c1, s1)
+    y2 = a8w4_gemm_prepared(ws, 70, k, c2, s2)
+    r1 = a8w4_gemm(x, c1, s1)
+    r2 = a8w4_gemm(x, c2, s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y1).view(np.uint16), host(r1).view(np.uint16))
+    assert np.array_equal(host(y2).view(np.uint16), host(r2).view(np.uint16))
+
+
 def test_a8_all_ones():
     torch = torch_cuda()
     k = 5120
