@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "lib")
 OUT = os.path.join(OUT_DIR, "libq4w.so")
 
-SOURCES = ["q4w_api.cpp", "q4_pack.hip", "q4_gemv.hip", "a8w4.hip"]
+SOURCES = ["q4w_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemv_mfma.hip", "a8w4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -33,6 +33,13 @@ DEVICE_FLAGS = [
     "-Wall",
     "-Wno-unused-function",
 ]
+
+# Per-source extra flags.  The matrix-core skinny kernel consumes every MFMA
+# result in VALU right away; the VGPR form of MFMA avoids copying each result
+# out of the accumulation registers (4 extra VALU ops per MFMA).
+EXTRA_FLAGS = {
+    "q4_gemv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _run(cmd, verbose):
@@ -58,7 +65,7 @@ def build(verbose=True, jobs=8):
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *DEVICE_FLAGS, *inc, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *DEVICE_FLAGS, *EXTRA_FLAGS.get(src, []), *inc, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -34,6 +34,7 @@
 //    workgroup to arrive (one kernel, deterministic, no cache flushes).
 
 #include "q4w_internal.h"
+#include "splitk.h"
 #include <hip/hip_fp16.h>
 
 namespace q4w {
@@ -77,11 +78,12 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 // Rows per lane: more rows re-use the activation registers more (less LDS
 // traffic per weight) at the cost of registers and of fewer workgroups.
-__host__ __device__ constexpr int rows_per_lane(int M) { return M == 1 ? 1 : (M <= 4 || M >= 7) ? 2 : 4; }
+// (This kernel serves M = 1..3; wider M goes to the matrix-core kernel.)
+__host__ __device__ constexpr int rows_per_lane(int M) { return M == 1 ? 1 : 2; }
 // Steps requested at once per wave (the register ring).
-__host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : M <= 4 ? 4 : 3; }
+__host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : 4; }
 // Occupancy target (waves per SIMD).
-__host__ __device__ constexpr int waves_per_simd(int M) { return M <= 3 ? 4 : M == 4 ? 3 : 2; }
+__host__ __device__ constexpr int waves_per_simd(int) { return 4; }
 
 namespace {
 
@@ -296,10 +298,7 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
     const int m = o / kRowsPerWg;
     const int n = tile_row0 + (o - m * kRowsPerWg);
     if (n < N) {
-      float s = 0.f;
-      for (int sp2 = 0; sp2 < S; ++sp2)
-        s += __hip_atomic_load(&partial[((size_t)sp2 * M + m) * N + n], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      const float s = sum_partials(&partial[(size_t)m * N + n], (size_t)M * N, S);
       y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(s));
     }
   }
@@ -343,7 +342,9 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
 // workgroups to fill the GPU.  split_k > 0 asks for that many slices (raised
 // when the LDS budget needs more).
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
+  if (M >= kMfmaMinM) return plan_skinny_mfma(M, N, K, split_k);
   SkinnyPlan p{};
+  p.route = kRouteDot2;
   p.rows_per_wg = kWaves * kSlots * rows_per_lane(M);
   p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
   const int nb = (int)(K / kBlock);
@@ -379,15 +380,11 @@ SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
                          uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p, void* ws,
                          hipStream_t s) {
+  if (p.route == kRouteMfma) return launch_skinny_mfma(x, codes, scales, y, M, N, K, p, ws, s);
   switch (M) {
     case 1: return launch_m<1>(x, codes, scales, y, N, K, p, ws, s);
     case 2: return launch_m<2>(x, codes, scales, y, N, K, p, ws, s);
     case 3: return launch_m<3>(x, codes, scales, y, N, K, p, ws, s);
-    case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
-    case 5: return launch_m<5>(x, codes, scales, y, N, K, p, ws, s);
-    case 6: return launch_m<6>(x, codes, scales, y, N, K, p, ws, s);
-    case 7: return launch_m<7>(x, codes, scales, y, N, K, p, ws, s);
-    case 8: return launch_m<8>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

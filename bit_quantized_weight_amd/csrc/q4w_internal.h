@@ -17,11 +17,19 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, uint8_t* codes,
                        uint16_t* scales, hipStream_t s);
 
 // ---- skinny (M <= 8) weight-streaming matmul ------------------------------
-// Split-K arrival counters: one uint32 per row tile (32 or 64 rows), in a
-// fixed region at the start of the workspace (16384 tiles: N <= 524,288).
-constexpr size_t kCounterRegionBytes = 64 * 1024;
-constexpr int64_t kMaxSkinnyN = int64_t(kCounterRegionBytes / 4) * 32;
+// Split-K arrival counters: one uint32 per row tile, in a fixed region at the
+// start of the workspace.  The smallest row tile is 8 rows, so 65536 counters
+// cover N <= 2^19.
+constexpr size_t kCounterRegionBytes = 256 * 1024;
+constexpr int kMinRowsPerTile = 8;
+constexpr int64_t kMaxSkinnyN = int64_t(1) << 19;
+static_assert(int64_t(kCounterRegionBytes / 4) * kMinRowsPerTile >= kMaxSkinnyN,
+              "one counter per row tile at the largest N");
+constexpr int kRouteDot2 = 0;     // VALU dot2 kernel (q4_gemv.hip)
+constexpr int kRouteMfma = 1;     // matrix-core kernel (q4_gemv_mfma.hip)
+constexpr int kMfmaMinM = 4;      // smallest M routed to the matrix cores
 struct SkinnyPlan {
+  int route;           // kRouteDot2 or kRouteMfma
   int rows_per_wg;     // output rows per workgroup
   int row_tiles;       // ceil(N / rows_per_wg)
   int splits;          // K slices
@@ -30,6 +38,10 @@ struct SkinnyPlan {
   size_t counter_bytes;
 };
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k);
+SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k);
+hipError_t launch_skinny_mfma(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                              uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
+                              void* ws, hipStream_t s);
 hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
                          uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
                          void* ws, hipStream_t s);

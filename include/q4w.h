@@ -80,7 +80,7 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
  *   order (deterministic: the same inputs give bit-identical outputs).
  *   ws / ws_bytes: device workspace of at least q4_gemv_skinny_ws_bytes(M, N,
  *   K, split_k) bytes (0 bytes when that function returns 0; ws may then be
- *   NULL).  Layout: a fixed 64 KiB region of per-tile arrival counters, then
+ *   NULL).  Layout: a fixed 256 KiB region of per-tile arrival counters, then
  *   fp32 partial sums.  The workspace must be zero-filled once before its
  *   first use; every completed call leaves the counter region zeroed again,
  *   so one workspace may serve any sequence of shapes (not concurrently).
