@@ -20,6 +20,9 @@
 //    buffer offset, which returns zeros without touching memory.
 //  * Activations are staged once per workgroup into LDS in a permuted fp16
 //    layout matching the in-register unpack below, plus a per-block bias.
+//    Their loads are issued before the weight loads: loads complete in issue
+//    order, and behind the weight stream of every other wave they would
+//    otherwise hold up the start of the compute.
 //  * Unpack: (w & 0x000F000F) ^ 0x64086408 flips each nibble's sign bit
 //    (two's complement q -> u = q + 8) and inserts the fp16 exponent of 1024
 //    (mantissa LSB = 1), giving the pair (1024 + u0, 1024 + u4) in one
@@ -84,6 +87,16 @@ __host__ __device__ constexpr int rows_per_lane(int M) { return M == 1 ? 1 : 2; 
 __host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : 4; }
 // Occupancy target (waves per SIMD).
 __host__ __device__ constexpr int waves_per_simd(int) { return 4; }
+// Largest slice (blocks): whole steps, within the LDS budget and at most two
+// rings long; and the (row, block) staging items per thread it needs.
+__host__ __device__ constexpr int max_slice_blocks(int M) {
+  return (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow < 2 * ring_steps(M) * kLanesPerRow
+             ? (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow
+             : 2 * ring_steps(M) * kLanesPerRow;
+}
+__host__ __device__ constexpr int stage_items(int M) {
+  return (M * max_slice_blocks(M) + kThreads - 1) / kThreads;
+}
 
 namespace {
 
@@ -143,8 +156,28 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
       sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kLanesPerRow * 2, 0);
     }
   };
-  // The weight loads go out before the activations are staged, so their HBM
-  // latency overlaps the staging.
+  // ---- activation loads first: items (row m, block b) of this slice -----
+  // They are needed before any weight step, and loads complete in issue
+  // order, so they go out ahead of the weight loads.  Blocks past the slice
+  // read zeros (out-of-range offset, no memory request).
+  constexpr int kItems = stage_items(M);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, 0, M * K * 2, kRsrcWord3);
+  uint4 raw[kItems][4];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int u = tid + it * kThreads;
+    const int m = u / bpad;
+    const int b = u - m * bpad;
+    const bool valid = u < M * bpad && b < nbs;
+    const uint32_t xo = valid ? (uint32_t)(m * K + (kb0 + b) * kBlock) * 2 : kOutOfRange;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
+      raw[it][q] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+
 #pragma unroll
   for (int p = 0; p < P; ++p) load_step(p, buf[p], sbuf[p]);
 
@@ -154,35 +187,30 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   // ---- stage the activation slice in the unpack's pair order --------------
   const uint32_t k1032 = 0x64086408u;   // fp16 pair (1032, 1032)
   const uint32_t k72 = 0x54805480u;     // fp16 pair (72, 72)
-  for (int u = tid; u < M * bpad; u += kThreads) {
-    const int m = u / bpad;
-    const int b = u - m * bpad;
-    uint4 raw[4];
-    if (b < nbs) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)(kb0 + b) * kBlock);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) raw[q] = src[q];
-    } else {
+  for (int it = 0; it < kItems; ++it) {
+    const int u = tid + it * kThreads;
+    if (u < M * bpad) {
+      const int m = u / bpad;
+      const int b = u - m * bpad;
+      float c = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) raw[q] = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        // raw holds elements e0..e7 of code word q as (e1:e0, e3:e2, e5:e4, e7:e6)
+        const uint32_t w0 = raw[it][q].x, w1 = raw[it][q].y, w2 = raw[it][q].z, w3 = raw[it][q].w;
+        uint4 o;
+        o.x = (w0 & 0xFFFFu) | (w2 << 16);                               // (e0, e4)
+        o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);                           // (e1, e5)
+        o.z = (w1 & 0xFFFFu) | (w3 << 16);                               // (e2, e6)
+        o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);                           // (e3, e7)
+        xs[(m * 4 + q) * bpad + b] = o;
+        c = dot2(o.x, k1032, c);
+        c = dot2(o.y, k72, c);
+        c = dot2(o.z, k1032, c);
+        c = dot2(o.w, k72, c);
+      }
+      cs[m * bpad + b] = -c;
     }
-    float c = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // raw[q] holds elements e0..e7 of code word q as (e1:e0, e3:e2, e5:e4, e7:e6)
-      const uint32_t w0 = raw[q].x, w1 = raw[q].y, w2 = raw[q].z, w3 = raw[q].w;
-      uint4 o;
-      o.x = (w0 & 0xFFFFu) | (w2 << 16);                               // (e0, e4)
-      o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);                           // (e1, e5)
-      o.z = (w1 & 0xFFFFu) | (w3 << 16);                               // (e2, e6)
-      o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);                           // (e3, e7)
-      xs[(m * 4 + q) * bpad + b] = o;
-      c = dot2(o.x, k1032, c);
-      c = dot2(o.y, k72, c);
-      c = dot2(o.z, k1032, c);
-      c = dot2(o.w, k72, c);
-    }
-    cs[m * bpad + b] = -c;
   }
   __syncthreads();
 
@@ -348,16 +376,14 @@ SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   p.rows_per_wg = kWaves * kSlots * rows_per_lane(M);
   p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
   const int nb = (int)(K / kBlock);
-  const int lds_blocks = kLdsBudget / (M * (4 * 16 + 4));      // blocks of one slice in LDS
+  const int lds_blocks = max_slice_blocks(M);                  // blocks of one slice in LDS
   int bps;
   if (split_k > 0) {
     bps = (nb + split_k - 1) / split_k;
-    const int cap = (lds_blocks / kLanesPerRow) * kLanesPerRow;
-    if (bps > cap) bps = cap;
+    if (bps > lds_blocks) bps = lds_blocks;
   } else {
     const int steps_total = (nb + kLanesPerRow - 1) / kLanesPerRow;
     int max_steps = lds_blocks / kLanesPerRow;
-    if (max_steps > 2 * ring_steps(M)) max_steps = 2 * ring_steps(M);
     if (max_steps < 1) max_steps = 1;
     int S = (steps_total + max_steps - 1) / max_steps;
     const int target_wgs = 1024;   // about four workgroups per CU on 256 CUs

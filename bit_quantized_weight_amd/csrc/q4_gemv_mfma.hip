@@ -37,11 +37,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLdsBudget = 48 * 1024;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kBlocksPerStep = 4;            // one 128-bit load per lane = 4 blocks per lane group set
 constexpr int kLdsBytesPerBlock = 64 * 16 + 16 * 4;   // A octets for 64 lanes + 16 biases
+constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks, 34 KB of LDS
+constexpr int kStageItems = kMaxSliceSteps * kBlocksPerStep * 16 / kThreads;   // (block, row) items per thread
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -75,15 +76,18 @@ __device__ __forceinline__ void transpose4(uint32_t (&v)[4]) {
 
 }  // namespace
 
-// Tiles of 16 rows per wave and steps in flight per wave.
+// Tiles of 16 rows per wave and steps in flight per wave.  Slices are at
+// most one ring long, so every load of a slice is issued at once: on MI355X
+// the stream only reaches full rate when each wave has all of its bytes in
+// flight.
 __host__ __device__ constexpr int mfma_tiles_per_wave(int) { return 1; }
-__host__ __device__ constexpr int mfma_ring_steps(int) { return 4; }
+__host__ __device__ constexpr int mfma_ring_steps(int) { return 8; }
 
 namespace {
 
 // kScaleQuad: K % 128 == 0, so the 4 scales of a step are one aligned 8-byte
 // load (otherwise four 2-byte loads).
-template <int M, bool kRing, bool kScaleQuad>
+template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads)
 mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
                    const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
@@ -124,7 +128,7 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
     vblk[i] = vrow[i] + grp;
   }
 
-  // Ring of P steps: codes (one 128-bit load per tile) and the 4 block
+  // P steps of loads: codes (one 128-bit load per tile) and the 4 block
   // scales of the step for this lane's row.
   uint4 buf[P][R];
   uint32_t sbuf[P][R][kBlocksPerStep];
@@ -151,6 +155,27 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
       }
     }
   };
+  // ---- activation loads first: (block b, row m) items of this slice ------
+  // Their data is needed before any weight step, and loads complete in issue
+  // order, so they go out ahead of the weight loads.  Rows m >= M and blocks
+  // past the slice read zeros (out-of-range offset, no memory request).
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, 0, M * K * 2, kRsrcWord3);
+  uint4 raw[kStageItems][4];
+#pragma unroll
+  for (int it = 0; it < kStageItems; ++it) {
+    const int u = tid + it * kThreads;
+    const int b = u >> 4;
+    const int m = u & 15;
+    const bool valid = m < M && b < nbs;
+    const uint32_t xo = valid ? (uint32_t)(m * K + (kb0 + b) * kBlock) * 2 : kOutOfRange;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
+      raw[it][q] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+
 #pragma unroll
   for (int p = 0; p < P; ++p) load_step(p, buf[p], sbuf[p]);
 
@@ -159,35 +184,30 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
   float* cl = reinterpret_cast<float*>(smem + bpad * 64);   // [bpad][16] -bias
   const uint32_t k1032 = 0x64086408u;
   const uint32_t k72 = 0x54805480u;
-  for (int u = tid; u < bpad * 16; u += kThreads) {
-    const int b = u >> 4;
-    const int m = u & 15;
-    uint4 raw[4];
-    if (m < M && b < nbs) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)(kb0 + b) * kBlock);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) raw[q] = src[q];
-    } else {
+  for (int it = 0; it < kStageItems; ++it) {
+    const int u = tid + it * kThreads;
+    if (u < bpad * 16) {
+      const int b = u >> 4;
+      const int m = u & 15;
+      float c = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) raw[q] = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 4; ++q) {
+        // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
+        const uint32_t w0 = raw[it][q].x, w1 = raw[it][q].y, w2 = raw[it][q].z, w3 = raw[it][q].w;
+        uint4 o;
+        o.x = (w0 & 0xFFFFu) | (w2 << 16);
+        o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
+        o.z = (w1 & 0xFFFFu) | (w3 << 16);
+        o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
+        xs[b * 64 + q * 16 + m] = o;
+        c = dot2(o.x, k1032, c);
+        c = dot2(o.y, k72, c);
+        c = dot2(o.z, k1032, c);
+        c = dot2(o.w, k72, c);
+      }
+      cl[b * 16 + m] = -c;
     }
-    float c = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
-      const uint32_t w0 = raw[q].x, w1 = raw[q].y, w2 = raw[q].z, w3 = raw[q].w;
-      uint4 o;
-      o.x = (w0 & 0xFFFFu) | (w2 << 16);
-      o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
-      o.z = (w1 & 0xFFFFu) | (w3 << 16);
-      o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
-      xs[b * 64 + q * 16 + m] = o;
-      c = dot2(o.x, k1032, c);
-      c = dot2(o.y, k72, c);
-      c = dot2(o.z, k1032, c);
-      c = dot2(o.w, k72, c);
-    }
-    cl[b * 16 + m] = -c;
   }
   __syncthreads();
 
@@ -205,6 +225,9 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
       w[i][3] = c[i].w;
       transpose4(w[i]);
     }
+    // All MFMAs of the step first, then their scale FMAs: the MFMA results
+    // are independent, so their latencies overlap.
+    f4 d4[kBlocksPerStep][R];
 #pragma unroll
     for (int j = 0; j < kBlocksPerStep; ++j) {
       const int b = t * kBlocksPerStep + j;
@@ -220,28 +243,23 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
         bw[1] = (u & 0x00F000F0u) ^ 0x54805480u;    // (64 + q + 8)   at k1, k5
         bw[2] = (u8 & 0x000F000Fu) ^ 0x64086408u;   // k2, k6
         bw[3] = (u8 & 0x00F000F0u) ^ 0x54805480u;   // k3, k7
-        const f4 d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, bw), cv, 0, 0, 0);
+        d4[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, bw), cv, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBlocksPerStep; ++j)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
         const float s = __half2float(__ushort_as_half((unsigned short)sc[i][j]));
 #pragma unroll
-        for (int r = 0; r < RM; ++r) yacc[i][r] = fmaf(d4[r], s, yacc[i][r]);
+        for (int r = 0; r < RM; ++r) yacc[i][r] = fmaf(d4[j][i][r], s, yacc[i][r]);
       }
-    }
   };
 
-  if (!kRing) {
+  // A slice is at most P steps (the plan guarantees it): no refills.
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      if (p < steps) compute_step(p, buf[p], sbuf[p]);
-  } else {
-#pragma unroll 1
-    for (int t0 = 0; t0 < steps; t0 += P) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (t0 + p < steps) compute_step(t0 + p, buf[p], sbuf[p]);
-        load_step(t0 + p + P, buf[p], sbuf[p]);
-      }
-    }
-  }
+  for (int p = 0; p < P; ++p)
+    if (p < steps) compute_step(p, buf[p], sbuf[p]);
 
   // ---- store: lane (col, grp) holds rows 4 grp + r of its column ---------
 #pragma unroll
@@ -296,22 +314,15 @@ hipError_t launch_mfma_m(const uint16_t* x, const uint8_t* codes, const uint16_t
     counters = reinterpret_cast<uint32_t*>(ws);
     partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes);
   }
-  const bool ring = bpad / kBlocksPerStep > mfma_ring_steps(M);
   const bool quad = (K / kBlock) % kBlocksPerStep == 0;
   const dim3 grid(p.row_tiles, p.splits);
   const uint4* c4 = reinterpret_cast<const uint4*>(codes);
   const int n = (int)N, k = (int)K, bps = p.blocks_per_split, S = p.splits;
-  if (ring && quad)
-    hipLaunchKernelGGL((mfma_skinny_kernel<M, true, true>), grid, dim3(kThreads), lds, s, x, c4,
-                       scales, y, partial, counters, n, k, bps, S);
-  else if (ring)
-    hipLaunchKernelGGL((mfma_skinny_kernel<M, true, false>), grid, dim3(kThreads), lds, s, x, c4,
-                       scales, y, partial, counters, n, k, bps, S);
-  else if (quad)
-    hipLaunchKernelGGL((mfma_skinny_kernel<M, false, true>), grid, dim3(kThreads), lds, s, x, c4,
+  if (quad)
+    hipLaunchKernelGGL((mfma_skinny_kernel<M, true>), grid, dim3(kThreads), lds, s, x, c4,
                        scales, y, partial, counters, n, k, bps, S);
   else
-    hipLaunchKernelGGL((mfma_skinny_kernel<M, false, false>), grid, dim3(kThreads), lds, s, x, c4,
+    hipLaunchKernelGGL((mfma_skinny_kernel<M, false>), grid, dim3(kThreads), lds, s, x, c4,
                        scales, y, partial, counters, n, k, bps, S);
   return hipGetLastError();
 }
@@ -319,8 +330,8 @@ hipError_t launch_mfma_m(const uint16_t* x, const uint8_t* codes, const uint16_t
 }  // namespace
 
 // Split plan of the matrix-core kernel: slices are whole 4-block steps, at
-// most two rings long and within the LDS budget, with enough slices to put
-// about four workgroups on every CU.
+// most one ring (kMaxSliceSteps) long, with enough slices to put about four
+// workgroups on every CU.
 SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
   SkinnyPlan p{};
   p.route = kRouteMfma;
@@ -328,14 +339,14 @@ SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
   p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
   const int nb = (int)(K / kBlock);
   const int steps_total = (nb + kBlocksPerStep - 1) / kBlocksPerStep;
-  const int lds_steps = kLdsBudget / (kLdsBytesPerBlock * kBlocksPerStep);
+  static_assert(kMaxSliceSteps <= mfma_ring_steps(0), "a slice fits the ring");
+  const int lds_steps = kMaxSliceSteps;
   int steps;
   if (split_k > 0) {
     steps = (steps_total + split_k - 1) / split_k;
     if (steps > lds_steps) steps = lds_steps;
   } else {
     int max_steps = lds_steps;
-    if (max_steps > 2 * mfma_ring_steps(M)) max_steps = 2 * mfma_ring_steps(M);
     int S = (steps_total + max_steps - 1) / max_steps;
     const int target_wgs = 1024;
     while ((int64_t)S * p.row_tiles < target_wgs && steps_total / (S + 1) >= 2) ++S;
