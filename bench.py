@@ -161,11 +161,18 @@ def bench_decode_step(torch, q4w, synthetic, reps, m=5):
     g = capture(torch, step.run)
     g.replay()
     t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
+    # the same step as one persistent launch over all 320 matmuls
+    step.plan_batched()
+    for _ in range(2):
+        step.run_batched()
+    t_batched = time_region(torch, lambda: [step.run_batched() for _ in range(reps)]) / reps
     total = step.weight_bytes + step.io_bytes
     out = dict(M=m, layers=len(step.layers), launches_per_step=step.launches,
                weight_bytes_per_step=step.weight_bytes, ms_graph=t_graph * 1e3,
                ms_eager=t_eager * 1e3, gbs_graph=total / t_graph / 1e9,
-               gbs_eager=total / t_eager / 1e9)
+               gbs_eager=total / t_eager / 1e9,
+               ms_batched=t_batched * 1e3, gbs_batched=total / t_batched / 1e9,
+               batched_grid=step.batch.plan.grid, batched_items=step.batch.plan.total_items)
     del g, step
     torch.cuda.empty_cache()
     return out

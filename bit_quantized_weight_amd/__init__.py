@@ -8,6 +8,7 @@ it has not been built.
 """
 
 from .binding import (  # noqa: F401
+    Batch,
     Q4WError,
     a8_quantize_act,
     a8w4_debug_block_acc,
@@ -15,6 +16,8 @@ from .binding import (  # noqa: F401
     a8w4_gemm_prepared,
     a8w4_prepare,
     a8w4_ws_bytes,
+    batched_plan,
+    batched_ws_bytes,
     gemv,
     gemv_ws_bytes,
     lib,

@@ -23,6 +23,18 @@ STATUS = {
 }
 
 
+class GemvDesc(ctypes.Structure):
+    """q4w_gemv_desc: one matmul of a batch."""
+    _fields_ = [("x", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class BatchedPlan(ctypes.Structure):
+    """q4w_batched_plan, filled by q4_gemv_batched_plan."""
+    _fields_ = [("M", ctypes.c_int), ("count", ctypes.c_int), ("total_items", ctypes.c_int),
+                ("grid", ctypes.c_int), ("variant", ctypes.c_int), ("ws", ctypes.c_void_p)]
+
+
 class Q4WError(RuntimeError):
     def __init__(self, fn, status, hip_err=0):
         self.status = status
@@ -63,6 +75,13 @@ def lib():
     L.a8w4_gemm_prepared.restype = i32
     L.a8w4_debug_block_acc.argtypes = [vp, vp, vp, i64, i64, i64, vp, sz, vp]
     L.a8w4_debug_block_acc.restype = i32
+    L.q4_gemv_batched_ws_bytes.argtypes = [i32, ctypes.POINTER(GemvDesc), i32]
+    L.q4_gemv_batched_ws_bytes.restype = sz
+    L.q4_gemv_batched_plan.argtypes = [i32, ctypes.POINTER(GemvDesc), i32, vp, sz,
+                                       ctypes.POINTER(BatchedPlan)]
+    L.q4_gemv_batched_plan.restype = i32
+    L.q4_gemv_batched_run.argtypes = [ctypes.POINTER(BatchedPlan), vp]
+    L.q4_gemv_batched_run.restype = i32
     L.q4w_status_str.argtypes = [i32]
     L.q4w_status_str.restype = ctypes.c_char_p
     L.q4w_last_hip_error.argtypes = []
@@ -209,3 +228,50 @@ def a8w4_debug_block_acc(x, codes, scales):
     _check("a8w4_debug_block_acc", lib().a8w4_debug_block_acc(
         _ptr(x), _ptr(codes), _ptr(acc), m, n, k, _ptr(ws), nb, _stream()))
     return acc
+
+
+class Batch:
+    """A planned batch of independent skinny matmuls (same M): the plan, its
+    workspace and references to every tensor it names (kept alive here)."""
+
+    def __init__(self, plan, ws, tensors):
+        self.plan = plan
+        self.ws = ws
+        self._tensors = tensors
+
+    def run(self):
+        """Enqueue the single persistent launch on torch's current stream."""
+        _check("q4_gemv_batched_run", lib().q4_gemv_batched_run(ctypes.byref(self.plan), _stream()))
+
+
+def _descs(items):
+    arr = (GemvDesc * len(items))()
+    for d, (x, codes, scales, y) in zip(arr, items):
+        d.x, d.codes, d.scales, d.y = x.data_ptr(), codes.data_ptr(), scales.data_ptr(), y.data_ptr()
+        d.N, d.K = codes.shape[0], x.shape[1]
+    return arr
+
+
+def batched_ws_bytes(m, items):
+    return lib().q4_gemv_batched_ws_bytes(m, _descs(items), len(items))
+
+
+def batched_plan(items):
+    """items: list of (x fp16 [M, K], codes, scales, y fp16 [M, N]) CUDA tensors, one M.
+    Plans them as one batch (blocking set-up call) and returns a Batch."""
+    import torch
+    m = items[0][0].shape[0]
+    for x, codes, scales, y in items:
+        _need(x, torch.float16, "x")
+        _need(y, torch.float16, "y")
+        if x.shape[0] != m or y.shape[0] != m:
+            raise ValueError("every matmul of a batch has the same M")
+    descs = _descs(items)
+    nb = lib().q4_gemv_batched_ws_bytes(m, descs, len(items))
+    if nb == 0:
+        raise ValueError("invalid batch shapes")
+    ws = torch.empty(nb, dtype=torch.uint8, device=items[0][0].device)
+    plan = BatchedPlan()
+    _check("q4_gemv_batched_plan", lib().q4_gemv_batched_plan(m, descs, len(items), _ptr(ws), nb,
+                                                              ctypes.byref(plan)))
+    return Batch(plan, ws, [t for it in items for t in it])

@@ -32,6 +32,10 @@
 #include "splitk.h"
 #include <hip/hip_fp16.h>
 
+#ifndef STREAM_P
+#define STREAM_P 8
+#endif
+
 namespace q4w {
 namespace {
 
@@ -40,9 +44,17 @@ constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kBlocksPerStep = 4;            // one 128-bit load per lane = 4 blocks per lane group set
-constexpr int kLdsBytesPerBlock = 64 * 16 + 16 * 4;   // A octets for 64 lanes + 16 biases
-constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks, 34 KB of LDS
-constexpr int kStageItems = kMaxSliceSteps * kBlocksPerStep * 16 / kThreads;   // (block, row) items per thread
+constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks
+// LDS per block of the slice: the M activation rows as A-operand octets
+// (4 slot groups x M rows x 16 bytes) and the -bias of rows 0..Mp4-1
+// (Mp4 = M rounded up to 4; rows >= M hold 0).  A-operand rows M..15 are
+// not stored: their lanes read a shared zero octet instead.
+__host__ __device__ constexpr int mp4(int M) { return (M + 3) / 4 * 4; }
+__host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * mp4(M); }
+constexpr int kLdsZeroBytes = 32;            // one zero octet + one zero float4
+__host__ __device__ constexpr int lds_bytes(int M, int bpad) {
+  return bpad * lds_bytes_per_block(M) + kLdsZeroBytes;
+}
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -85,24 +97,24 @@ __host__ __device__ constexpr int mfma_ring_steps(int) { return 8; }
 
 namespace {
 
+// One work item: row tile `tile` (64 rows) x K-slice `split` of one matmul.
 // kScaleQuad: K % 128 == 0, so the 4 scales of a step are one aligned 8-byte
-// load (otherwise four 2-byte loads).
+// load (otherwise four 2-byte loads).  The LDS of the previous item of this
+// workgroup is overwritten only after a barrier.
 template <int M, bool kScaleQuad>
-__global__ void __launch_bounds__(kThreads)
-mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
-                   const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-                   float* __restrict__ partial, uint32_t* __restrict__ counters,
-                   int N, int K, int bps, int S) {
+__device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
+                                          const uint4* __restrict__ codes,
+                                          const uint16_t* __restrict__ scales,
+                                          uint16_t* __restrict__ y, float* __restrict__ partial,
+                                          uint32_t* __restrict__ counters, int N, int K, int bps,
+                                          int S, int tile, int split, uint4* smem) {
   constexpr int R = mfma_tiles_per_wave(M);
   constexpr int P = mfma_ring_steps(M);
   constexpr int kRowsPerWg = kWaves * R * 16;
   constexpr int RM = M < 4 ? M : 4;          // D rows a lane accumulates
-  extern __shared__ uint4 smem[];
 
   const int nb = K / kBlock;
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
   const int kb0 = split * bps;
   const int nbs = min(bps, nb - kb0);
   const int steps = (nbs + kBlocksPerStep - 1) / kBlocksPerStep;
@@ -161,55 +173,64 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
   // past the slice read zeros (out-of-range offset, no memory request).
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, 0, M * K * 2, kRsrcWord3);
-  uint4 raw[kStageItems][4];
-#pragma unroll
-  for (int it = 0; it < kStageItems; ++it) {
-    const int u = tid + it * kThreads;
-    const int b = u >> 4;
-    const int m = u & 15;
-    const bool valid = m < M && b < nbs;
-    const uint32_t xo = valid ? (uint32_t)(m * K + (kb0 + b) * kBlock) * 2 : kOutOfRange;
+  // One (block, row) item per thread: bpad x Mp4 <= 32 x 8 items.
+  static_assert(kMaxSliceSteps * kBlocksPerStep * mp4(8) <= kThreads, "one staging item per thread");
+  constexpr int MP = mp4(M);
+  const int sb = tid / MP;                 // staging block
+  const int sm = tid % MP;                 // staging row
+  uint4 raw[4];
+  {
+    const bool valid = sm < M && sb < nbs;
+    const uint32_t xo = valid ? (uint32_t)(sm * K + (kb0 + sb) * kBlock) * 2 : kOutOfRange;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
-      raw[it][q] = make_uint4(v[0], v[1], v[2], v[3]);
+      raw[q] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
 
 #pragma unroll
   for (int p = 0; p < P; ++p) load_step(p, buf[p], sbuf[p]);
 
-  // ---- stage A operands and biases: xs[b][g][m] (16 rows, M..15 zero) -----
-  uint4* xs = smem;
-  float* cl = reinterpret_cast<float*>(smem + bpad * 64);   // [bpad][16] -bias
+  // ---- stage A operands and biases: xs[b][g][m] (m < M), cl[b][m] ---------
+  __syncthreads();   // the previous item of this workgroup is done with the LDS
+  char* lds = reinterpret_cast<char*>(smem);
+  uint4* xs = smem;                                                    // [bpad][4][M]
+  float* cl = reinterpret_cast<float*>(lds + bpad * 64 * M);           // [bpad][MP]
+  const int zero_off = bpad * lds_bytes_per_block(M);                  // zero octet, zero float4
   const uint32_t k1032 = 0x64086408u;
   const uint32_t k72 = 0x54805480u;
+  if (sb < bpad) {
+    float c = 0.f;
 #pragma unroll
-  for (int it = 0; it < kStageItems; ++it) {
-    const int u = tid + it * kThreads;
-    if (u < bpad * 16) {
-      const int b = u >> 4;
-      const int m = u & 15;
-      float c = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
-        const uint32_t w0 = raw[it][q].x, w1 = raw[it][q].y, w2 = raw[it][q].z, w3 = raw[it][q].w;
-        uint4 o;
-        o.x = (w0 & 0xFFFFu) | (w2 << 16);
-        o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
-        o.z = (w1 & 0xFFFFu) | (w3 << 16);
-        o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
-        xs[b * 64 + q * 16 + m] = o;
-        c = dot2(o.x, k1032, c);
-        c = dot2(o.y, k72, c);
-        c = dot2(o.z, k1032, c);
-        c = dot2(o.w, k72, c);
-      }
-      cl[b * 16 + m] = -c;
+    for (int q = 0; q < 4; ++q) {
+      // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
+      const uint32_t w0 = raw[q].x, w1 = raw[q].y, w2 = raw[q].z, w3 = raw[q].w;
+      uint4 o;
+      o.x = (w0 & 0xFFFFu) | (w2 << 16);
+      o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
+      o.z = (w1 & 0xFFFFu) | (w3 << 16);
+      o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
+      if (sm < M) xs[(sb * 4 + q) * M + sm] = o;
+      c = dot2(o.x, k1032, c);
+      c = dot2(o.y, k72, c);
+      c = dot2(o.z, k1032, c);
+      c = dot2(o.w, k72, c);
     }
+    cl[sb * MP + sm] = -c;                 // rows >= M read zeros, so c == 0 there
   }
+  if (tid < 2) reinterpret_cast<uint4*>(lds + zero_off)[tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
+
+  // Per-lane LDS addresses: A octet of block b at a_base + b * a_stride
+  // (rows >= M: the zero octet, stride 0), bias float4 of rows 4 grp.. at
+  // c_base + b * c_stride (groups past Mp4: the zero float4).
+  const bool a_live = col < M;
+  const int a_base = a_live ? (grp * M + col) * 16 : zero_off;
+  const int a_stride = a_live ? 64 * M : 0;
+  const bool c_live = 4 * grp < MP;
+  const int c_base = c_live ? bpad * 64 * M + grp * 16 : zero_off + 16;
+  const int c_stride = c_live ? MP * 4 : 0;
 
   f4 yacc[R];
 #pragma unroll
@@ -231,8 +252,8 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
 #pragma unroll
     for (int j = 0; j < kBlocksPerStep; ++j) {
       const int b = t * kBlocksPerStep + j;
-      const uint4 av = xs[b * 64 + lane];
-      const f4 cv = reinterpret_cast<const f4*>(cl)[b * 4 + grp];
+      const uint4 av = *reinterpret_cast<const uint4*>(lds + a_base + b * a_stride);
+      const f4 cv = *reinterpret_cast<const f4*>(lds + c_base + b * c_stride);
       const h8 a = __builtin_bit_cast(h8, av);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -302,19 +323,247 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
     __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int M, bool kScaleQuad>
+__global__ void __launch_bounds__(kThreads)
+mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
+                   const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
+                   float* __restrict__ partial, uint32_t* __restrict__ counters,
+                   int N, int K, int bps, int S) {
+  extern __shared__ uint4 smem[];
+  mfma_item<M, kScaleQuad>(x, codes, scales, y, partial, counters, N, K, bps, S, blockIdx.x,
+                           blockIdx.y, smem);
+}
+
+// Streaming form: one persistent launch computes every matmul of a table
+// (same M).  Work items are 64-row tiles over the whole of K (no split-K:
+// no partials, no arrival counters, no waits on store completion); a
+// workgroup walks items w, w + gridDim.x, ... as a sequence of chunks of
+// kMaxSliceSteps steps and issues the loads of chunk c + 1 (weights, scales
+// and activations, into the other register set) before it computes chunk c,
+// so its loads are in flight while it stages and computes.  Activations of
+// a chunk go to one of two LDS buffers; one barrier per chunk.
+// Steps per chunk of the streaming kernel: two chunks of loads stay in
+// registers (no spills at 3 waves per SIMD).
+__host__ __device__ constexpr int stream_steps(bool quad) { return quad ? STREAM_P : 4; }
+
+struct Walker {
+  int item;      // work item (row tile of matmul g)
+  int g;         // matmul index
+  int chunk;     // chunk along K
+  int nchunks;   // chunks of this matmul
+  bool valid;
+};
+
+template <int M, bool kScaleQuad>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_items) {
+  constexpr int P = stream_steps(kScaleQuad);
+  constexpr int kChunkBlocks = P * kBlocksPerStep;
+  constexpr int MP = mp4(M);
+  constexpr int RM = M < 4 ? M : 4;
+  constexpr int kLdsBuf = lds_bytes(M, kChunkBlocks);
+  constexpr int kZeroOff = kChunkBlocks * lds_bytes_per_block(M);
+  extern __shared__ uint4 smem[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int sb = tid / MP;                 // staging block of this thread
+  const int sm = tid % MP;                 // staging row of this thread
+  const int rl = wave * 16 + col;          // tile-local weight row of this lane
+
+  // Per-lane LDS addresses (see mfma_item), for a buffer of kChunkBlocks blocks.
+  const bool a_live = col < M;
+  const int a_base = a_live ? (grp * M + col) * 16 : kZeroOff;
+  const int a_stride = a_live ? 64 * M : 0;
+  const bool c_live = 4 * grp < MP;
+  const int c_base = c_live ? kChunkBlocks * 64 * M + grp * 16 : kZeroOff + 16;
+  const int c_stride = c_live ? MP * 4 : 0;
+
+  auto start = [&](Walker& w, int item) {
+    w.item = item;
+    w.valid = item < total_items;
+    if (!w.valid) return;
+    while (w.g + 1 < count && item >= table[w.g + 1].item_begin) ++w.g;
+    w.chunk = 0;
+    w.nchunks = (table[w.g].K / kBlock + kChunkBlocks - 1) / kChunkBlocks;
+  };
+  auto advance = [&](const Walker& w) {
+    Walker n = w;
+    if (w.chunk + 1 < w.nchunks) {
+      ++n.chunk;
+    } else {
+      start(n, w.item + (int)gridDim.x);
+    }
+    return n;
+  };
+
+  // One register set: a chunk's codes, scales and this thread's activation item.
+  // Scales: with kScaleQuad one 8-byte load per step, kept packed (two fp16
+  // per register); otherwise four 2-byte loads per step.
+  constexpr int kScaleRegs = kScaleQuad ? 2 : kBlocksPerStep;
+  struct Set {
+    uint4 w[P];
+    uint32_t s[P][kScaleRegs];
+    uint4 x[4];
+  };
+  auto issue = [&](const Walker& w, Set& st) {
+    const BatchedGemv& d = table[w.valid ? w.g : 0];
+    const int nb = d.K / kBlock;
+    const int kb0 = w.chunk * kChunkBlocks;
+    const int nbs = w.valid ? min(kChunkBlocks, nb - kb0) : 0;
+    const int tile = w.item - d.item_begin;
+    const int tile_row0 = tile * 64;
+    const int rows_here = w.valid ? min(64, d.N - tile_row0) : 0;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(d.codes + (size_t)(w.valid ? tile_row0 : 0) * nb), 0, rows_here * nb * kBlockBytes,
+        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(d.scales + (size_t)(w.valid ? tile_row0 : 0) * nb), 0, rows_here * nb * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)d.x, 0, w.valid ? M * d.K * 2 : 0, kRsrcWord3);
+    {
+      const bool valid = sm < M && sb < nbs;
+      const uint32_t xo = valid ? (uint32_t)(sm * d.K + (kb0 + sb) * kBlock) * 2 : kOutOfRange;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
+        st.x[q] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    const uint32_t vrow = (uint32_t)(rl * nb + kb0);
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      const bool live = t * kBlocksPerStep + grp < nbs;
+      const bool slive = t * kBlocksPerStep < nbs;
+      const uint32_t vo = live ? (vrow + grp) * kBlockBytes : kOutOfRange;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kBlocksPerStep * kBlockBytes, 0);
+      st.w[t] = make_uint4(v[0], v[1], v[2], v[3]);
+      const uint32_t so = slive ? vrow * 2 : kOutOfRange;
+      if constexpr (kScaleQuad) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, so, t * kBlocksPerStep * 2, 0);
+        st.s[t][0] = v2[0];
+        st.s[t][1] = v2[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kBlocksPerStep; ++j)
+          st.s[t][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kBlocksPerStep * 2 + 2 * j, 0);
+      }
+    }
+  };
+  auto scale_of = [&](const Set& st, int t, int j) -> float {
+    uint32_t bits;
+    if constexpr (kScaleQuad) bits = (j & 1) ? (st.s[t][j >> 1] >> 16) : (st.s[t][j >> 1] & 0xFFFFu);
+    else bits = st.s[t][j];
+    return __half2float(__ushort_as_half((unsigned short)bits));
+  };
+
+  f4 yacc = f4{0.f, 0.f, 0.f, 0.f};
+  auto process = [&](const Walker& w, const Set& st, char* lds) {
+    const BatchedGemv& d = table[w.g];
+    const int nb = d.K / kBlock;
+    const int nbs = min(kChunkBlocks, nb - w.chunk * kChunkBlocks);
+    const int steps = (nbs + kBlocksPerStep - 1) / kBlocksPerStep;
+    // stage this chunk's activations (blocks past the chunk are zeros)
+    if (sb < kChunkBlocks) {
+      uint4* xs = reinterpret_cast<uint4*>(lds);
+      float* cl = reinterpret_cast<float*>(lds + kChunkBlocks * 64 * M);
+      float c = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = st.x[q].x, w1 = st.x[q].y, w2 = st.x[q].z, w3 = st.x[q].w;
+        uint4 o;
+        o.x = (w0 & 0xFFFFu) | (w2 << 16);
+        o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
+        o.z = (w1 & 0xFFFFu) | (w3 << 16);
+        o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
+        if (sm < M) xs[(sb * 4 + q) * M + sm] = o;
+        c = dot2(o.x, 0x64086408u, c);
+        c = dot2(o.y, 0x54805480u, c);
+        c = dot2(o.z, 0x64086408u, c);
+        c = dot2(o.w, 0x54805480u, c);
+      }
+      cl[sb * MP + sm] = -c;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      if (t < steps) {
+        uint32_t wv[4] = {st.w[t].x, st.w[t].y, st.w[t].z, st.w[t].w};
+        transpose4(wv);
+        f4 d4[kBlocksPerStep];
+#pragma unroll
+        for (int j = 0; j < kBlocksPerStep; ++j) {
+          const int b = t * kBlocksPerStep + j;
+          const h8 a = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(lds + a_base + b * a_stride));
+          const f4 cv = *reinterpret_cast<const f4*>(lds + c_base + b * c_stride);
+          const uint32_t u = wv[j];
+          const uint32_t u8 = u >> 8;
+          v4u bw;
+          bw[0] = (u & 0x000F000Fu) ^ 0x64086408u;
+          bw[1] = (u & 0x00F000F0u) ^ 0x54805480u;
+          bw[2] = (u8 & 0x000F000Fu) ^ 0x64086408u;
+          bw[3] = (u8 & 0x00F000F0u) ^ 0x54805480u;
+          d4[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(h8, bw), cv, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kBlocksPerStep; ++j) {
+          const float sc = scale_of(st, t, j);
+#pragma unroll
+          for (int r = 0; r < RM; ++r) yacc[r] = fmaf(d4[j][r], sc, yacc[r]);
+        }
+      }
+    }
+    if (w.chunk + 1 == w.nchunks) {          // item done: store its 64 x M outputs
+      const int n = (w.item - d.item_begin) * 64 + rl;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int m = 4 * grp + r;
+        if (m < M && n < d.N) d.y[(size_t)m * d.N + n] = __half_as_ushort(__float2half_rn(yacc[r]));
+      }
+      yacc = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // zero octet and zero float4 of both LDS buffers
+  if (tid < 4)
+    reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + (tid >> 1) * kLdsBuf + kZeroOff)[tid & 1] =
+        make_uint4(0, 0, 0, 0);
+  char* lds0 = reinterpret_cast<char*>(smem);
+  char* lds1 = lds0 + kLdsBuf;
+
+  Set s0, s1;
+  Walker cur{};
+  cur.g = 0;
+  start(cur, blockIdx.x);
+  issue(cur, s0);
+  while (cur.valid) {
+    const Walker nxt = advance(cur);
+    issue(nxt, s1);
+    process(cur, s0, lds0);
+    if (!nxt.valid) break;
+    const Walker nn = advance(nxt);
+    issue(nn, s0);
+    process(nxt, s1, lds1);
+    cur = nn;
+  }
+}
+
 template <int M>
 hipError_t launch_mfma_m(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
                          uint16_t* y, int64_t N, int64_t K, const SkinnyPlan& p, void* ws,
                          hipStream_t s) {
   const int bpad = ((p.blocks_per_split + kBlocksPerStep - 1) / kBlocksPerStep) * kBlocksPerStep;
-  const size_t lds = (size_t)bpad * kLdsBytesPerBlock;
+  const size_t lds = (size_t)lds_bytes(M, bpad);
   uint32_t* counters = nullptr;
   float* partial = nullptr;
   if (p.splits > 1) {
     counters = reinterpret_cast<uint32_t*>(ws);
     partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes);
   }
-  const bool quad = (K / kBlock) % kBlocksPerStep == 0;
+  const bool quad = (K / kBlock) % kBlocksPerStep == 0 && ((uintptr_t)scales & 7) == 0;
   const dim3 grid(p.row_tiles, p.splits);
   const uint4* c4 = reinterpret_cast<const uint4*>(codes);
   const int n = (int)N, k = (int)K, bps = p.blocks_per_split, S = p.splits;
@@ -360,6 +609,92 @@ SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
     p.ws_bytes = p.counter_bytes + (size_t)p.splits * M * N * sizeof(float);
   }
   return p;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The streaming kernel's work items are 64-row tiles over the whole of K.
+static int64_t stream_tiles(int64_t N) { return (N + 63) / 64; }
+
+BatchedLayout batched_layout(int /*M*/, int count, const int64_t* N, const int64_t* /*K*/) {
+  BatchedLayout L{};
+  for (int g = 0; g < count; ++g) L.total_items += stream_tiles(N[g]);
+  L.table_bytes = align256((size_t)count * sizeof(BatchedGemv));
+  L.total_bytes = L.table_bytes;
+  return L;
+}
+
+void batched_fill_table(int /*M*/, int count, const uint16_t* const* x,
+                        const uint8_t* const* codes, const uint16_t* const* scales,
+                        uint16_t* const* y, const int64_t* N, const int64_t* K, void* /*ws*/,
+                        BatchedGemv* table) {
+  int64_t item = 0;
+  for (int g = 0; g < count; ++g) {
+    BatchedGemv& d = table[g];
+    d = BatchedGemv{};
+    d.x = x[g];
+    d.codes = reinterpret_cast<const uint4*>(codes[g]);
+    d.scales = scales[g];
+    d.y = y[g];
+    d.N = (int)N[g];
+    d.K = (int)K[g];
+    d.bps = (int)(K[g] / kBlock);
+    d.S = 1;
+    d.item_begin = (int)item;
+    item += stream_tiles(N[g]);
+  }
+}
+
+namespace {
+template <int M>
+const void* batched_kernel_ptr(bool quad) {
+  return quad ? reinterpret_cast<const void*>(&mfma_stream_kernel<M, true>)
+              : reinterpret_cast<const void*>(&mfma_stream_kernel<M, false>);
+}
+
+// LDS of the streaming kernel: two chunk buffers.
+int batched_lds(int M, bool quad) { return 2 * lds_bytes(M, stream_steps(quad) * kBlocksPerStep); }
+
+const void* batched_kernel_for(int M, bool quad) {
+  switch (M) {
+    case 1: return batched_kernel_ptr<1>(quad);
+    case 2: return batched_kernel_ptr<2>(quad);
+    case 3: return batched_kernel_ptr<3>(quad);
+    case 4: return batched_kernel_ptr<4>(quad);
+    case 5: return batched_kernel_ptr<5>(quad);
+    case 6: return batched_kernel_ptr<6>(quad);
+    case 7: return batched_kernel_ptr<7>(quad);
+    case 8: return batched_kernel_ptr<8>(quad);
+    default: return nullptr;
+  }
+}
+}  // namespace
+
+bool batched_quad(int count, const int64_t* K, const uint16_t* const* scales) {
+  for (int g = 0; g < count; ++g)
+    if ((K[g] / kBlock) % kBlocksPerStep != 0 || ((uintptr_t)scales[g] & 7) != 0) return false;
+  return true;
+}
+
+int batched_grid(int M, bool quad, int64_t total_items) {
+  const void* k = batched_kernel_for(M, quad);
+  int per_cu = 0, cus = 0, dev = 0;
+  if (!k || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, batched_lds(M, quad)) != hipSuccess)
+    return 0;
+  int64_t grid = (int64_t)per_cu * cus;
+  if (grid > total_items) grid = total_items;
+  return (int)(grid < 1 ? 1 : grid);
+}
+
+hipError_t launch_batched(int M, bool quad, const void* ws, int count, int total_items,
+                          int grid, hipStream_t s) {
+  const void* k = batched_kernel_for(M, quad);
+  if (!k) return hipErrorInvalidValue;
+  const BatchedGemv* table = static_cast<const BatchedGemv*>(ws);
+  void* args[] = {(void*)&table, (void*)&count, (void*)&total_items};
+  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, batched_lds(M, quad), s);
 }
 
 hipError_t launch_skinny_mfma(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,

@@ -5,6 +5,9 @@
 #include "q4w.h"
 #include "q4w_internal.h"
 
+#include <climits>
+#include <vector>
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -21,6 +24,31 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;  // kernels index rows and columns
 // The skinny kernel addresses one workgroup's rows (<= 64 x K/2 bytes) through
 // a buffer resource with a 32-bit byte range.
 constexpr int64_t kMaxSkinnyK = int64_t(1) << 24;
+
+constexpr int kMaxBatch = 1 << 20;
+
+// Sizes and shapes of a batch (pointers are not looked at).
+int check_batch_shapes(int M, const q4w_gemv_desc* d, int count) {
+  if (!d || count < 1 || count > kMaxBatch) return Q4W_ERR_INVALID_ARG;
+  if (M < 1 || M > 8) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  for (int g = 0; g < count; ++g) {
+    if (d[g].N <= 0 || d[g].K <= 0) return Q4W_ERR_INVALID_ARG;
+    if (d[g].K % q4w::kBlock != 0 || d[g].N > q4w::kMaxSkinnyN || d[g].K > kMaxSkinnyK)
+      return Q4W_ERR_UNSUPPORTED_SHAPE;
+  }
+  return Q4W_OK;
+}
+
+q4w::BatchedLayout batch_layout(int M, const q4w_gemv_desc* d, int count,
+                                std::vector<int64_t>& N, std::vector<int64_t>& K) {
+  N.resize(count);
+  K.resize(count);
+  for (int g = 0; g < count; ++g) {
+    N[g] = d[g].N;
+    K[g] = d[g].K;
+  }
+  return q4w::batched_layout(M, count, N.data(), K.data());
+}
 
 }  // namespace
 
@@ -159,5 +187,64 @@ const char* q4w_status_str(int status) {
 }
 
 int q4w_last_hip_error(void) { return g_last_hip_error; }
+
+size_t q4_gemv_batched_ws_bytes(int M, const q4w_gemv_desc* descs, int count) {
+  if (check_batch_shapes(M, descs, count) != Q4W_OK) return 0;
+  std::vector<int64_t> N, K;
+  return batch_layout(M, descs, count, N, K).total_bytes;
+}
+
+int q4_gemv_batched_plan(int M, const q4w_gemv_desc* descs, int count, void* ws, size_t ws_bytes,
+                         q4w_batched_plan* plan) {
+  if (!plan) return Q4W_ERR_INVALID_ARG;
+  const int st = check_batch_shapes(M, descs, count);
+  if (st != Q4W_OK) return st;
+  for (int g = 0; g < count; ++g) {
+    const q4w_gemv_desc& e = descs[g];
+    if (!e.x || !e.codes || !e.scales || !e.y) return Q4W_ERR_INVALID_ARG;
+    if (!aligned(e.x, 16) || !aligned(e.codes, 16) || !aligned(e.scales, 2) || !aligned(e.y, 4))
+      return Q4W_ERR_MISALIGNED;
+  }
+  std::vector<int64_t> N, K;
+  const q4w::BatchedLayout L = batch_layout(M, descs, count, N, K);
+  if (L.total_items > INT_MAX) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (!ws || ws_bytes < L.total_bytes) return Q4W_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  std::vector<const uint16_t*> x(count), scales(count);
+  std::vector<const uint8_t*> codes(count);
+  std::vector<uint16_t*> y(count);
+  for (int g = 0; g < count; ++g) {
+    x[g] = descs[g].x;
+    codes[g] = descs[g].codes;
+    scales[g] = descs[g].scales;
+    y[g] = descs[g].y;
+  }
+  std::vector<q4w::BatchedGemv> table(count);
+  q4w::batched_fill_table(M, count, x.data(), codes.data(), scales.data(), y.data(), N.data(),
+                          K.data(), ws, table.data());
+  hipError_t e = hipMemcpy(ws, table.data(), count * sizeof(q4w::BatchedGemv),
+                           hipMemcpyHostToDevice);
+  if (e == hipSuccess && L.counter_bytes > 0)
+    e = hipMemset(static_cast<char*>(ws) + L.table_bytes, 0, L.counter_bytes);
+  if (e != hipSuccess) return hip_status(e);
+  const bool quad = q4w::batched_quad(count, K.data(), scales.data());
+  const int grid = q4w::batched_grid(M, quad, L.total_items);
+  if (grid < 1) return hip_status(hipErrorInvalidDeviceFunction);
+  plan->M = M;
+  plan->variant = quad ? 1 : 0;
+  plan->count = count;
+  plan->total_items = (int)L.total_items;
+  plan->grid = grid;
+  plan->ws = ws;
+  return Q4W_OK;
+}
+
+int q4_gemv_batched_run(const q4w_batched_plan* plan, hipStream_t stream) {
+  if (!plan || !plan->ws || plan->M < 1 || plan->M > 8 || plan->count < 1 ||
+      plan->total_items < 1 || plan->grid < 1 || plan->variant < 0 || plan->variant > 1)
+    return Q4W_ERR_INVALID_ARG;
+  return hip_status(q4w::launch_batched(plan->M, plan->variant == 1, plan->ws, plan->count,
+                                        plan->total_items, plan->grid, stream));
+}
 
 }  // extern "C"

@@ -48,6 +48,39 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t
 
 hipError_t launch_fill_zero_u16(uint16_t* y, int64_t count, hipStream_t s);
 
+// ---- batched skinny matmuls (one persistent launch) ------------------------
+// Device-side table entry: one matmul of the batch (the streaming kernel
+// uses x, codes, scales, y, N, K and item_begin).
+struct BatchedGemv {
+  const uint16_t* x;
+  const uint4* codes;
+  const uint16_t* scales;
+  uint16_t* y;
+  float* partial;       // S x M x N fp32 split-K partials (S > 1)
+  uint32_t* counters;   // one arrival counter per row tile (S > 1)
+  int N, K, bps, S;
+  int item_begin;       // index of this matmul's first work item
+  int pad[3];
+};
+static_assert(sizeof(BatchedGemv) == 80, "table entry layout");
+
+struct BatchedLayout {
+  size_t table_bytes, counter_bytes, partial_bytes, total_bytes;
+  int64_t total_items;
+};
+// Workspace layout of a batch: the table (256-byte aligned).
+BatchedLayout batched_layout(int M, int count, const int64_t* N, const int64_t* K);
+// Fills `table` (host memory, count entries) for a workspace at device address ws.
+void batched_fill_table(int M, int count, const uint16_t* const* x, const uint8_t* const* codes,
+                        const uint16_t* const* scales, uint16_t* const* y, const int64_t* N,
+                        const int64_t* K, void* ws, BatchedGemv* table);
+// Whether every matmul of a batch takes its 4 step scales in one 8-byte load.
+bool batched_quad(int count, const int64_t* K, const uint16_t* const* scales);
+// Persistent workgroups to launch for a batch of total_items items.
+int batched_grid(int M, bool quad, int64_t total_items);
+hipError_t launch_batched(int M, bool quad, const void* ws, int count, int total_items, int grid,
+                          hipStream_t s);
+
 // ---- A8 prefill -----------------------------------------------------------
 constexpr int kA8TileM = 32;      // rows per MFMA tile of the private activation layout
 

@@ -10,7 +10,9 @@ down 17408 -> 5120.  Weights are synthetic (seeded) and packed on the GPU.
 
 The projections of a step are independent here (each reads its own input
 buffer), so the pass measures the weight stream itself; a model would chain
-them through its mixers.
+them through its mixers.  ``run`` issues one skinny matmul per projection;
+``run_batched`` computes the same outputs with one persistent launch over
+all of them (planned once by ``plan_batched``).
 """
 
 from . import binding, synthetic
@@ -46,6 +48,7 @@ class DecodeStep:
         nbytes = max(binding.gemv_ws_bytes(m, n, k, 0) for _, k, n in synthetic.LAYER_PROJECTIONS)
         self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         self.io_bytes = layers * sum(2 * m * k + 2 * m * n for _, k, n in synthetic.LAYER_PROJECTIONS)
+        self.batch = None
 
     @property
     def launches(self):
@@ -56,3 +59,17 @@ class DecodeStep:
         for layer, projs in enumerate(self.layers):
             for pi, (codes, scales) in enumerate(projs):
                 binding.q4_gemv_skinny_raw(self.xs[pi], codes, scales, self.ys[layer][pi], 0, self.ws)
+
+    def plan_batched(self):
+        """Plan every projection of the step as one batch (a blocking set-up call)."""
+        items = [(self.xs[pi], codes, scales, self.ys[layer][pi])
+                 for layer, projs in enumerate(self.layers)
+                 for pi, (codes, scales) in enumerate(projs)]
+        self.batch = binding.batched_plan(items)
+        return self.batch
+
+    def run_batched(self):
+        """Enqueue the whole step as one persistent launch on the current stream."""
+        if self.batch is None:
+            self.plan_batched()
+        self.batch.run()

@@ -148,6 +148,65 @@ int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
                          int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Batched skinny matmuls: one persistent launch computes a whole list of
+ * independent y_g = x_g . What_g^T (same M for all, 1 <= M <= 8), e.g. every
+ * projection of every layer of one decode step, which the pages' decode
+ * streams once per token ("Qwen3.8-27B at 256K on a 24GB RTX PRO 4000 SFF",
+ * page 3, the paragraph on weight streaming during decode).  Work items of
+ * all matmuls are streamed back to back by resident workgroups, so the
+ * weight stream does not drain and refill between matmuls.
+ *
+ * Work items are 64-row tiles over the whole of K (no split-K); each
+ * workgroup keeps the loads of its next chunk of weights in flight while it
+ * computes the current one.  Results are deterministic (a fixed summation
+ * order: repeated runs are bit-identical) and agree with q4_gemv_skinny to
+ * the stated tolerance, not bit for bit (different K split).  The matmuls
+ * are independent: no y_g may overlap any x_h, codes_h, scales_h or other
+ * y_h of the batch.  A batch should hold many row tiles (N/64 summed over
+ * the batch well above the number of CUs); a single small matmul is better
+ * served by q4_gemv_skinny.
+ *
+ * q4w_gemv_desc: one matmul, layouts and alignments as for q4_gemv_skinny;
+ *   N >= 1, K >= 32, K % 32 == 0, N <= 2^19, K <= 2^24.
+ * q4_gemv_batched_ws_bytes: workspace bytes for the batch (its work
+ *   table); 0 if a size or shape is invalid.
+ * q4_gemv_batched_plan: a set-up call, not for graph capture.  Checks every
+ *   descriptor, writes the device-side work table into ws (256-byte
+ *   aligned, >= q4_gemv_batched_ws_bytes bytes) and fills *plan.  It synchronizes with the device (blocking copy); the
+ *   descriptor array may be freed when it returns.  The workspace then
+ *   belongs to the plan until the caller stops using the plan.
+ *   Errors: INVALID_ARG (null, count < 1, N or K <= 0), UNSUPPORTED_SHAPE,
+ *   MISALIGNED, WORKSPACE, HIP.
+ * q4_gemv_batched_run: enqueues the single persistent launch on `stream`
+ *   (capturable in a HIP graph); every y_g is complete when the stream
+ *   reaches the next command.  Runs of one plan must not overlap in time.
+ *   The inputs named by the descriptors are read at run time, so new x_g
+ *   contents are picked up by the next run.
+ */
+typedef struct q4w_gemv_desc {
+  const uint16_t* x;       /* [M, K] fp16 */
+  const uint8_t* codes;    /* [N, K/2] */
+  const uint16_t* scales;  /* [N, K/32] fp16 */
+  uint16_t* y;             /* [M, N] fp16 */
+  int64_t N;
+  int64_t K;
+} q4w_gemv_desc;
+
+typedef struct q4w_batched_plan {
+  int M;
+  int count;
+  int total_items;         /* work items of the batch */
+  int grid;                /* persistent workgroups launched */
+  int variant;             /* kernel variant chosen at plan time */
+  void* ws;                /* the workspace holding the table */
+} q4w_batched_plan;
+
+size_t q4_gemv_batched_ws_bytes(int M, const q4w_gemv_desc* descs, int count);
+int q4_gemv_batched_plan(int M, const q4w_gemv_desc* descs, int count, void* ws,
+                         size_t ws_bytes, q4w_batched_plan* plan);
+int q4_gemv_batched_run(const q4w_batched_plan* plan, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* q4w_status_str(int status);
 

@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ["q4_pack", "q4_gemv_skinny", "q4_gemv_skinny_ws_bytes", "a8_quantize_act",
               "a8w4_gemm_prefill", "a8w4_ws_bytes", "a8w4_debug_block_acc",
               "a8w4_prepare_act", "a8w4_gemm_prepared",
+              "q4_gemv_batched_ws_bytes", "q4_gemv_batched_plan", "q4_gemv_batched_run",
               "q4w_status_str", "q4w_last_hip_error"]:
         assert n in names, n
 
@@ -150,3 +151,50 @@ def test_binding_loads_lazily_and_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def _descs(entries):
+    arr = (binding.GemvDesc * len(entries))()
+    for d, (x, c, s, y, n, k) in zip(arr, entries):
+        d.x, d.codes, d.scales, d.y, d.N, d.K = x, c, s, y, n, k
+    return arr
+
+
+def test_batched_checks(L):
+    """Every argument check of the batched entry points returns before any HIP
+    call (a valid batch would upload its table, so none is planned here)."""
+    good = (A, A, A, A, 5120, 17408)
+    ws_bytes = L.q4_gemv_batched_ws_bytes
+    plan = binding.BatchedPlan()
+    pl = ctypes.byref(plan)
+    one = _descs([good])
+    assert ws_bytes(5, one, 1) > 0
+    assert ws_bytes(5, one, 0) == 0 and ws_bytes(0, one, 1) == 0 and ws_bytes(9, one, 1) == 0
+    assert ws_bytes(5, None, 1) == 0
+    assert ws_bytes(5, _descs([(A, A, A, A, 64, 48)]), 1) == 0       # K % 32
+    assert ws_bytes(5, _descs([(A, A, A, A, 0, 64)]), 1) == 0        # N == 0
+    # two matmuls need at least the sum of their split-K workspaces
+    two = _descs([good, (A, A, A, A, 7168, 5120)])
+    assert ws_bytes(5, two, 2) >= ws_bytes(5, one, 1)
+    bp = L.q4_gemv_batched_plan
+    need = ws_bytes(5, one, 1)
+    assert bp(5, one, 1, p(A), need, None) == INVALID                # no plan struct
+    assert bp(5, None, 1, p(A), need, pl) == INVALID
+    assert bp(5, one, 0, p(A), need, pl) == INVALID
+    assert bp(0, one, 1, p(A), need, pl) == SHAPE
+    assert bp(9, one, 1, p(A), need, pl) == SHAPE
+    assert bp(5, _descs([(A, A, A, A, -1, 64)]), 1, p(A), need, pl) == INVALID
+    assert bp(5, _descs([(A, A, A, A, 64, 0)]), 1, p(A), need, pl) == INVALID
+    assert bp(5, _descs([(A, A, A, A, 64, 96 + 16)]), 1, p(A), need, pl) == SHAPE
+    assert bp(5, _descs([(A, A, A, A, 1 << 20, 64)]), 1, p(A), need, pl) == SHAPE   # N > 2^19
+    assert bp(5, _descs([(0, A, A, A, 64, 64)]), 1, p(A), need, pl) == INVALID     # null x
+    assert bp(5, _descs([(U, A, A, A, 64, 64)]), 1, p(A), need, pl) == ALIGN       # x not 16-aligned
+    assert bp(5, _descs([(A, U, A, A, 64, 64)]), 1, p(A), need, pl) == ALIGN
+    assert bp(5, _descs([(A, A, A + 1, A, 64, 64)]), 1, p(A), need, pl) == ALIGN
+    assert bp(5, _descs([(A, A, A, U, 64, 64)]), 1, p(A), need, pl) == ALIGN       # y not 4-aligned
+    assert bp(5, one, 1, None, need, pl) == WS
+    assert bp(5, one, 1, p(A), need - 1, pl) == WS
+    assert bp(5, one, 1, p(A + 16), need, pl) == ALIGN
+    run = L.q4_gemv_batched_run
+    assert run(None, NUL) == INVALID
+    assert run(ctypes.byref(binding.BatchedPlan()), NUL) == INVALID  # never planned

@@ -70,3 +70,43 @@ def test_decode_step_graph_replay_matches_eager(step):
             for pi in range(len(synthetic.LAYER_PROJECTIONS)):
                 assert np.array_equal(host(step.ys[layer][pi]).view(np.uint16),
                                       eager[layer][pi].view(np.uint16)), (rep, layer, pi)
+
+
+def test_decode_step_batched(step):
+    """The whole step as one persistent launch: sampled rows of three layers
+    against the oracle, then three graph replays of the batched launch, each
+    bit-identical to the first batched run."""
+    torch = torch_cuda()
+    step.plan_batched()
+    for ys in step.ys:
+        for y in ys:
+            y.fill_(7.0)
+    step.run_batched()
+    torch.cuda.synchronize()
+    xs = [host(x) for x in step.xs]
+    for layer in CHECK_LAYERS:
+        for pi, (name, k, n) in enumerate(synthetic.LAYER_PROJECTIONS):
+            rows = _rows(n, 10 * layer + pi)
+            q, d = q4.quantize(step.kept[(layer, pi)])
+            assert_close(host(step.ys[layer][pi])[:, rows], q4.matmul(xs[pi], q, d),
+                         what=f"batched layer {layer} {name}")
+    first = {(l, pi): host(step.ys[l][pi]).copy() for l in (0, 17, 63)
+             for pi in range(len(synthetic.LAYER_PROJECTIONS))}
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run_batched()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step.run_batched()
+    for rep in range(3):
+        for ys in step.ys:
+            for y in ys:
+                y.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (l, pi), ref in first.items():
+            assert np.array_equal(host(step.ys[l][pi]).view(np.uint16), ref.view(np.uint16)), (rep, l, pi)

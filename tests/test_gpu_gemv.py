@@ -204,3 +204,59 @@ def test_large_n_split_counters(m):
     x = synthetic.activations(m, k, 79 + m)
     y = run(x, codes, scales, split_k=2)
     assert_close(y[:, rows], q4.matmul(x, q, d), what=f"N={n} M={m} split 2")
+
+
+BATCH_SHAPES = [(100, 96), (300, 1056), (257, 5120), (70, 8192), (5120, 17408), (64, 512)]
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 5, 8])
+def test_batched_matches_oracle_and_repeats(m):
+    """One persistent launch over six matmuls of mixed, ragged shapes (K not
+    a multiple of 128 included): each output within the bar of the oracle,
+    and repeated runs of the plan bit-identical (fixed summation order)."""
+    torch = torch_cuda()
+    from bit_quantized_weight_amd import batched_plan
+    items, refs = [], []
+    for i, (n, k) in enumerate(BATCH_SHAPES):
+        codes, scales, q, d = packed(n, k, 900 + i)
+        x = synthetic.activations(m, k, 950 + i)
+        y = torch.full((m, n), 7.0, dtype=torch.float16, device="cuda")
+        items.append((dev(x, torch), codes, scales, y))
+        refs.append(q4.matmul(x, q, d))
+    batch = batched_plan(items)
+    first = None
+    for rep in range(3):
+        for it in items:
+            it[3].fill_(7.0)
+        batch.run()
+        torch.cuda.synchronize()
+        outs = [host(it[3]).copy() for it in items]
+        for (n, k), got, ref in zip(BATCH_SHAPES, outs, refs):
+            assert_close(got, ref, what=f"batched M={m} N={n} K={k} rep {rep}")
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), m
+
+
+def test_batched_aligned_and_ragged_k_variants():
+    """A batch whose every K is a multiple of 128 takes the packed-scale
+    kernel variant; adding one ragged K switches the whole batch to the
+    other variant.  Both agree with the oracle."""
+    torch = torch_cuda()
+    from bit_quantized_weight_amd import batched_plan
+    for shapes in ([(96, 1024), (300, 5120)], [(96, 1024), (300, 5120), (70, 1056)]):
+        items, refs = [], []
+        for i, (n, k) in enumerate(shapes):
+            codes, scales, q, d = packed(n, k, 960 + i)
+            x = synthetic.activations(5, k, 970 + i)
+            items.append((dev(x, torch), codes, scales,
+                          torch.empty((5, n), dtype=torch.float16, device="cuda")))
+            refs.append(q4.matmul(x, q, d))
+        batch = batched_plan(items)
+        assert batch.plan.variant == (1 if len(shapes) == 2 else 0)
+        batch.run()
+        torch.cuda.synchronize()
+        for (n, k), it, ref in zip(shapes, items, refs):
+            assert_close(host(it[3]), ref, what=f"variant test N={n} K={k}")
