@@ -35,6 +35,12 @@
 #ifndef STREAM_P
 #define STREAM_P 8
 #endif
+#ifndef STREAM_WAVES
+#define STREAM_WAVES 2
+#endif
+#ifndef STREAM_SETS
+#define STREAM_SETS 2
+#endif
 
 namespace q4w {
 namespace {
@@ -355,7 +361,7 @@ struct Walker {
 };
 
 template <int M, bool kScaleQuad>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(STREAM_WAVES, 8)))
 mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_items) {
   constexpr int P = stream_steps(kScaleQuad);
   constexpr int kChunkBlocks = P * kBlocksPerStep;
@@ -532,22 +538,32 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + (tid >> 1) * kLdsBuf + kZeroOff)[tid & 1] =
         make_uint4(0, 0, 0, 0);
   char* lds0 = reinterpret_cast<char*>(smem);
-  char* lds1 = lds0 + kLdsBuf;
 
-  Set s0, s1;
-  Walker cur{};
-  cur.g = 0;
-  start(cur, blockIdx.x);
-  issue(cur, s0);
-  while (cur.valid) {
-    const Walker nxt = advance(cur);
-    issue(nxt, s1);
-    process(cur, s0, lds0);
-    if (!nxt.valid) break;
-    const Walker nn = advance(nxt);
-    issue(nn, s0);
-    process(nxt, s1, lds1);
-    cur = nn;
+  // Ring of kSets register sets: while chunk c is computed, chunks
+  // c + 1 .. c + kSets - 1 are in flight.
+  constexpr int kSets = STREAM_SETS;
+  Set sets[kSets];
+  Walker w[kSets];
+  w[0] = Walker{};
+  start(w[0], blockIdx.x);
+  issue(w[0], sets[0]);
+#pragma unroll
+  for (int i = 1; i < kSets; ++i) {
+    w[i] = advance(w[i - 1]);
+    issue(w[i], sets[i]);
+  }
+  int parity = 0;
+  while (w[0].valid) {
+#pragma unroll
+    for (int i = 0; i < kSets; ++i) {
+      if (w[i].valid) {
+        process(w[i], sets[i], lds0 + parity * kLdsBuf);
+        parity ^= 1;
+        const Walker nw = advance(w[(i + kSets - 1) % kSets]);
+        issue(nw, sets[i]);
+        w[i] = nw;
+      }
+    }
   }
 }
 
