@@ -32,14 +32,16 @@
 #include "splitk.h"
 #include <hip/hip_fp16.h>
 
+// Streaming kernel shape (measured best on the 64-layer decode step at M = 1
+// and 5): 4-step chunks, 3 waves per SIMD, 4 row tiles per work item.
 #ifndef STREAM_P
-#define STREAM_P 8
+#define STREAM_P 4
 #endif
 #ifndef STREAM_WAVES
-#define STREAM_WAVES 2
+#define STREAM_WAVES 3
 #endif
-#ifndef STREAM_SETS
-#define STREAM_SETS 2
+#ifndef STREAM_TILES
+#define STREAM_TILES 4
 #endif
 
 namespace q4w {
@@ -341,21 +343,25 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
 }
 
 // Streaming form: one persistent launch computes every matmul of a table
-// (same M).  Work items are 64-row tiles over the whole of K (no split-K:
-// no partials, no arrival counters, no waits on store completion); a
-// workgroup walks items w, w + gridDim.x, ... as a sequence of chunks of
-// kMaxSliceSteps steps and issues the loads of chunk c + 1 (weights, scales
-// and activations, into the other register set) before it computes chunk c,
-// so its loads are in flight while it stages and computes.  Activations of
-// a chunk go to one of two LDS buffers; one barrier per chunk.
-// Steps per chunk of the streaming kernel: two chunks of loads stay in
-// registers (no spills at 3 waves per SIMD).
+// (same M).  A work item is kStreamTiles row tiles of 64 rows over the whole
+// of K (no split-K: no partials, no arrival counters, no waits on store
+// completion).  A workgroup walks items w, w + gridDim.x, ... as a sequence
+// of units (K-chunk c, tile t), tile innermost: the activations of chunk c
+// are staged into LDS once (one barrier) and serve all tiles of the item.
+// The loads of the next unit (codes, scales, and activations at tile 0) go
+// into the other register set before the current unit is computed, so each
+// wave keeps a chunk of weights in flight while it stages and computes.
+// Two LDS activation buffers alternate by chunk.
+// Steps per chunk of the streaming kernel (two chunks of loads stay in
+// registers) and 64-row tiles per work item.
 __host__ __device__ constexpr int stream_steps(bool quad) { return quad ? STREAM_P : 4; }
+constexpr int kStreamTiles = STREAM_TILES;
 
 struct Walker {
-  int item;      // work item (row tile of matmul g)
+  int item;      // work item of matmul g
   int g;         // matmul index
   int chunk;     // chunk along K
+  int tile;      // tile within the item
   int nchunks;   // chunks of this matmul
   bool valid;
 };
@@ -364,11 +370,14 @@ template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(STREAM_WAVES, 8)))
 mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_items) {
   constexpr int P = stream_steps(kScaleQuad);
+  constexpr int T = kStreamTiles;
   constexpr int kChunkBlocks = P * kBlocksPerStep;
   constexpr int MP = mp4(M);
   constexpr int RM = M < 4 ? M : 4;
   constexpr int kLdsBuf = lds_bytes(M, kChunkBlocks);
   constexpr int kZeroOff = kChunkBlocks * lds_bytes_per_block(M);
+  constexpr int kSets = 2;
+  static_assert(T % kSets == 0, "units cycle through register sets and tiles together");
   extern __shared__ uint4 smem[];
 
   const int tid = threadIdx.x;
@@ -394,21 +403,26 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     if (!w.valid) return;
     while (w.g + 1 < count && item >= table[w.g + 1].item_begin) ++w.g;
     w.chunk = 0;
+    w.tile = 0;
     w.nchunks = (table[w.g].K / kBlock + kChunkBlocks - 1) / kChunkBlocks;
   };
   auto advance = [&](const Walker& w) {
     Walker n = w;
-    if (w.chunk + 1 < w.nchunks) {
+    if (w.tile + 1 < T) {
+      ++n.tile;
+    } else if (w.chunk + 1 < w.nchunks) {
       ++n.chunk;
+      n.tile = 0;
     } else {
       start(n, w.item + (int)gridDim.x);
     }
     return n;
   };
 
-  // One register set: a chunk's codes, scales and this thread's activation item.
-  // Scales: with kScaleQuad one 8-byte load per step, kept packed (two fp16
-  // per register); otherwise four 2-byte loads per step.
+  // One register set: a unit's codes and scales, and this thread's
+  // activation item (loaded at tile 0 only).  Scales: with kScaleQuad one
+  // 8-byte load per step, kept packed (two fp16 per register); otherwise
+  // four 2-byte loads per step.
   constexpr int kScaleRegs = kScaleQuad ? 2 : kBlocksPerStep;
   struct Set {
     uint4 w[P];
@@ -420,16 +434,15 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     const int nb = d.K / kBlock;
     const int kb0 = w.chunk * kChunkBlocks;
     const int nbs = w.valid ? min(kChunkBlocks, nb - kb0) : 0;
-    const int tile = w.item - d.item_begin;
-    const int tile_row0 = tile * 64;
-    const int rows_here = w.valid ? min(64, d.N - tile_row0) : 0;
+    const int tile_row0 = ((w.item - d.item_begin) * T + w.tile) * 64;
+    const int rows_here = w.valid ? max(0, min(64, d.N - tile_row0)) : 0;
+    const size_t row0 = rows_here > 0 ? (size_t)tile_row0 : 0;
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(d.codes + (size_t)(w.valid ? tile_row0 : 0) * nb), 0, rows_here * nb * kBlockBytes,
-        kRsrcWord3);
+        (void*)(d.codes + row0 * nb), 0, rows_here * nb * kBlockBytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(d.scales + (size_t)(w.valid ? tile_row0 : 0) * nb), 0, rows_here * nb * 2, kRsrcWord3);
+        (void*)(d.scales + row0 * nb), 0, rows_here * nb * 2, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)d.x, 0, w.valid ? M * d.K * 2 : 0, kRsrcWord3);
+        (void*)d.x, 0, w.valid && w.tile == 0 ? M * d.K * 2 : 0, kRsrcWord3);
     {
       const bool valid = sm < M && sb < nbs;
       const uint32_t xo = valid ? (uint32_t)(sm * d.K + (kb0 + sb) * kBlock) * 2 : kOutOfRange;
@@ -466,13 +479,8 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     return __half2float(__ushort_as_half((unsigned short)bits));
   };
 
-  f4 yacc = f4{0.f, 0.f, 0.f, 0.f};
-  auto process = [&](const Walker& w, const Set& st, char* lds) {
-    const BatchedGemv& d = table[w.g];
-    const int nb = d.K / kBlock;
-    const int nbs = min(kChunkBlocks, nb - w.chunk * kChunkBlocks);
-    const int steps = (nbs + kBlocksPerStep - 1) / kBlocksPerStep;
-    // stage this chunk's activations (blocks past the chunk are zeros)
+  // stage a chunk's activations into an LDS buffer (blocks past it are zeros)
+  auto stage = [&](const Set& st, char* lds) {
     if (sb < kChunkBlocks) {
       uint4* xs = reinterpret_cast<uint4*>(lds);
       float* cl = reinterpret_cast<float*>(lds + kChunkBlocks * 64 * M);
@@ -493,7 +501,14 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
       }
       cl[sb * MP + sm] = -c;
     }
-    __syncthreads();
+  };
+
+  // compute a unit into one tile's accumulators; store them after the last chunk
+  auto compute = [&](const Walker& w, const Set& st, const char* lds, f4& yacc) {
+    const BatchedGemv& d = table[w.g];
+    const int nb = d.K / kBlock;
+    const int nbs = min(kChunkBlocks, nb - w.chunk * kChunkBlocks);
+    const int steps = (nbs + kBlocksPerStep - 1) / kBlocksPerStep;
 #pragma unroll
     for (int t = 0; t < P; ++t) {
       if (t < steps) {
@@ -522,8 +537,8 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
         }
       }
     }
-    if (w.chunk + 1 == w.nchunks) {          // item done: store its 64 x M outputs
-      const int n = (w.item - d.item_begin) * 64 + rl;
+    if (w.chunk + 1 == w.nchunks) {          // this tile is done: store its 64 x M outputs
+      const int n = ((w.item - d.item_begin) * T + w.tile) * 64 + rl;
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
         const int m = 4 * grp + r;
@@ -539,11 +554,11 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
         make_uint4(0, 0, 0, 0);
   char* lds0 = reinterpret_cast<char*>(smem);
 
-  // Ring of kSets register sets: while chunk c is computed, chunks
-  // c + 1 .. c + kSets - 1 are in flight.
-  constexpr int kSets = STREAM_SETS;
   Set sets[kSets];
   Walker w[kSets];
+  f4 yacc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) yacc[t] = f4{0.f, 0.f, 0.f, 0.f};
   w[0] = Walker{};
   start(w[0], blockIdx.x);
   issue(w[0], sets[0]);
@@ -552,16 +567,23 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     w[i] = advance(w[i - 1]);
     issue(w[i], sets[i]);
   }
-  int parity = 0;
+  // Units arrive tile 0, 1, ..., T-1 per chunk, so unit u of each round of
+  // T units is tile u and uses register set u % kSets (all static).
+  int parity = 1;
   while (w[0].valid) {
 #pragma unroll
-    for (int i = 0; i < kSets; ++i) {
-      if (w[i].valid) {
-        process(w[i], sets[i], lds0 + parity * kLdsBuf);
-        parity ^= 1;
-        const Walker nw = advance(w[(i + kSets - 1) % kSets]);
-        issue(nw, sets[i]);
-        w[i] = nw;
+    for (int u = 0; u < T; ++u) {
+      Walker& cw = w[u % kSets];
+      if (cw.valid) {
+        if (u == 0) {                        // a new chunk: stage its activations
+          parity ^= 1;
+          stage(sets[u % kSets], lds0 + parity * kLdsBuf);
+          __syncthreads();
+        }
+        compute(cw, sets[u % kSets], lds0 + parity * kLdsBuf, yacc[u]);
+        const Walker nw = advance(w[(u + kSets - 1) % kSets]);
+        issue(nw, sets[u % kSets]);
+        cw = nw;
       }
     }
   }
@@ -629,8 +651,8 @@ SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// The streaming kernel's work items are 64-row tiles over the whole of K.
-static int64_t stream_tiles(int64_t N) { return (N + 63) / 64; }
+// The streaming kernel's work items: kStreamTiles 64-row tiles over the whole of K.
+static int64_t stream_tiles(int64_t N) { return (N + 64 * kStreamTiles - 1) / (64 * kStreamTiles); }
 
 BatchedLayout batched_layout(int /*M*/, int count, const int64_t* N, const int64_t* /*K*/) {
   BatchedLayout L{};
