@@ -33,9 +33,9 @@
 #include <hip/hip_fp16.h>
 
 // Streaming kernel shape (measured best on the 64-layer decode step at M = 1
-// and 5): 4-step chunks, 3 waves per SIMD, 4 row tiles per work item.
+// and 5): 8-step chunks, 3 waves per SIMD, 4 row tiles per work item.
 #ifndef STREAM_P
-#define STREAM_P 4
+#define STREAM_P 8
 #endif
 #ifndef STREAM_WAVES
 #define STREAM_WAVES 3
@@ -419,17 +419,20 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     return n;
   };
 
-  // One register set: a unit's codes and scales, and this thread's
-  // activation item (loaded at tile 0 only).  Scales: with kScaleQuad one
-  // 8-byte load per step, kept packed (two fp16 per register); otherwise
-  // four 2-byte loads per step.
-  constexpr int kScaleRegs = kScaleQuad ? 2 : kBlocksPerStep;
+  // One register set: a unit's codes and scales.  Scales with kScaleQuad:
+  // lane group g loads the 4 scales of step 4l + g of its row (8 bytes), one
+  // load per 4 steps; the groups' words are all-gathered with permlane swaps
+  // at compute time.  Otherwise four 2-byte loads per step.
+  static_assert(P % kBlocksPerStep == 0, "scale loads cover 4 steps each");
+  constexpr int kScaleLoads = P / kBlocksPerStep;
   struct Set {
     uint4 w[P];
-    uint32_t s[P][kScaleRegs];
-    uint4 x[4];
+    uint32_t s[kScaleQuad ? kScaleLoads : P][kScaleQuad ? 2 : kBlocksPerStep];
   };
-  auto issue = [&](const Walker& w, Set& st) {
+  // This thread's activation item of the next chunk (loaded with the chunk's
+  // tile-0 unit, consumed when that chunk is staged).
+  uint4 xbuf[4];
+  auto issue = [&](const Walker& w, Set& st, bool with_x) {
     const BatchedGemv& d = table[w.valid ? w.g : 0];
     const int nb = d.K / kBlock;
     const int kb0 = w.chunk * kChunkBlocks;
@@ -441,53 +444,66 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
         (void*)(d.codes + row0 * nb), 0, rows_here * nb * kBlockBytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(d.scales + row0 * nb), 0, rows_here * nb * 2, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)d.x, 0, w.valid && w.tile == 0 ? M * d.K * 2 : 0, kRsrcWord3);
-    {
+    if (with_x) {
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)d.x, 0, w.valid ? M * d.K * 2 : 0, kRsrcWord3);
       const bool valid = sm < M && sb < nbs;
       const uint32_t xo = valid ? (uint32_t)(sm * d.K + (kb0 + sb) * kBlock) * 2 : kOutOfRange;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
-        st.x[q] = make_uint4(v[0], v[1], v[2], v[3]);
+        xbuf[q] = make_uint4(v[0], v[1], v[2], v[3]);
       }
     }
     const uint32_t vrow = (uint32_t)(rl * nb + kb0);
 #pragma unroll
     for (int t = 0; t < P; ++t) {
       const bool live = t * kBlocksPerStep + grp < nbs;
-      const bool slive = t * kBlocksPerStep < nbs;
       const uint32_t vo = live ? (vrow + grp) * kBlockBytes : kOutOfRange;
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kBlocksPerStep * kBlockBytes, 0);
       st.w[t] = make_uint4(v[0], v[1], v[2], v[3]);
-      const uint32_t so = slive ? vrow * 2 : kOutOfRange;
-      if constexpr (kScaleQuad) {
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, so, t * kBlocksPerStep * 2, 0);
-        st.s[t][0] = v2[0];
-        st.s[t][1] = v2[1];
-      } else {
+    }
+    if constexpr (kScaleQuad) {
+#pragma unroll
+      for (int l = 0; l < kScaleLoads; ++l) {
+        const int t = l * kBlocksPerStep + grp;     // the step whose scales this lane loads
+        const uint32_t so = t * kBlocksPerStep < nbs ? (vrow + t * kBlocksPerStep) * 2 : kOutOfRange;
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0);
+        st.s[l][0] = v2[0];
+        st.s[l][1] = v2[1];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < P; ++t) {
+        const uint32_t so = t * kBlocksPerStep < nbs ? vrow * 2 : kOutOfRange;
 #pragma unroll
         for (int j = 0; j < kBlocksPerStep; ++j)
           st.s[t][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kBlocksPerStep * 2 + 2 * j, 0);
       }
     }
   };
-  auto scale_of = [&](const Set& st, int t, int j) -> float {
-    uint32_t bits;
-    if constexpr (kScaleQuad) bits = (j & 1) ? (st.s[t][j >> 1] >> 16) : (st.s[t][j >> 1] & 0xFFFFu);
-    else bits = st.s[t][j];
-    return __half2float(__ushort_as_half((unsigned short)bits));
+  // Value of lane group g's v in every lane: out[g].
+  auto all_gather4 = [](uint32_t v, uint32_t (&out)[4]) {
+    uint32_t x = v, y = v;
+    swap32(x, y);            // x: groups (0, 1, 0, 1), y: (2, 3, 2, 3)
+    uint32_t a = x, b = x, c = y, e = y;
+    swap16(a, b);            // a: group 0 everywhere, b: group 1
+    swap16(c, e);            // c: group 2, e: group 3
+    out[0] = a;
+    out[1] = b;
+    out[2] = c;
+    out[3] = e;
   };
 
   // stage a chunk's activations into an LDS buffer (blocks past it are zeros)
-  auto stage = [&](const Set& st, char* lds) {
+  auto stage = [&](char* lds) {
     if (sb < kChunkBlocks) {
       uint4* xs = reinterpret_cast<uint4*>(lds);
       float* cl = reinterpret_cast<float*>(lds + kChunkBlocks * 64 * M);
       float c = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = st.x[q].x, w1 = st.x[q].y, w2 = st.x[q].z, w3 = st.x[q].w;
+        const uint32_t w0 = xbuf[q].x, w1 = xbuf[q].y, w2 = xbuf[q].z, w3 = xbuf[q].w;
         uint4 o;
         o.x = (w0 & 0xFFFFu) | (w2 << 16);
         o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
@@ -509,6 +525,26 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
     const int nb = d.K / kBlock;
     const int nbs = min(kChunkBlocks, nb - w.chunk * kChunkBlocks);
     const int steps = (nbs + kBlocksPerStep - 1) / kBlocksPerStep;
+    // scales of step t, block j: quad -> word (j >> 1) of lane group (t % 4)
+    // of load t / 4, half (j & 1)
+    uint32_t sg[kScaleQuad ? kScaleLoads : 1][2][4];
+    if constexpr (kScaleQuad) {
+#pragma unroll
+      for (int l = 0; l < kScaleLoads; ++l) {
+        all_gather4(st.s[l][0], sg[l][0]);
+        all_gather4(st.s[l][1], sg[l][1]);
+      }
+    }
+    auto scale_of = [&](int t, int j) -> float {
+      uint32_t bits;
+      if constexpr (kScaleQuad) {
+        const uint32_t wd = sg[t / kBlocksPerStep][j >> 1][t % kBlocksPerStep];
+        bits = (j & 1) ? (wd >> 16) : (wd & 0xFFFFu);
+      } else {
+        bits = st.s[t][j];
+      }
+      return __half2float(__ushort_as_half((unsigned short)bits));
+    };
 #pragma unroll
     for (int t = 0; t < P; ++t) {
       if (t < steps) {
@@ -531,7 +567,7 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
         }
 #pragma unroll
         for (int j = 0; j < kBlocksPerStep; ++j) {
-          const float sc = scale_of(st, t, j);
+          const float sc = scale_of(t, j);
 #pragma unroll
           for (int r = 0; r < RM; ++r) yacc[r] = fmaf(d4[j][r], sc, yacc[r]);
         }
@@ -561,11 +597,11 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
   for (int t = 0; t < T; ++t) yacc[t] = f4{0.f, 0.f, 0.f, 0.f};
   w[0] = Walker{};
   start(w[0], blockIdx.x);
-  issue(w[0], sets[0]);
+  issue(w[0], sets[0], true);
 #pragma unroll
   for (int i = 1; i < kSets; ++i) {
     w[i] = advance(w[i - 1]);
-    issue(w[i], sets[i]);
+    issue(w[i], sets[i], i % T == 0);
   }
   // Units arrive tile 0, 1, ..., T-1 per chunk, so unit u of each round of
   // T units is tile u and uses register set u % kSets (all static).
@@ -577,12 +613,12 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
       if (cw.valid) {
         if (u == 0) {                        // a new chunk: stage its activations
           parity ^= 1;
-          stage(sets[u % kSets], lds0 + parity * kLdsBuf);
+          stage(lds0 + parity * kLdsBuf);
           __syncthreads();
         }
         compute(cw, sets[u % kSets], lds0 + parity * kLdsBuf, yacc[u]);
         const Walker nw = advance(w[(u + kSets - 1) % kSets]);
-        issue(nw, sets[u % kSets]);
+        issue(nw, sets[u % kSets], (u + kSets) % T == 0);   // tile 0 of the next chunk
         cw = nw;
       }
     }
