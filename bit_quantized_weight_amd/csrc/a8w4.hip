@@ -154,11 +154,11 @@ __global__ void __launch_bounds__(64) act_quant_tiled_kernel(const uint16_t* __r
 }
 
 // ---- int8 MFMA GEMM --------------------------------------------------------
-// MFMA and VALU instructions do not overlap on gfx950 (measured), so the
-// kernel minimizes VALU work per MFMA: the nibble -> int8 unpack and the
-// weight-scale preparation are done once per workgroup into LDS, and the
-// per-output rescale is the three-FMA magic-number form (1.5 FMAs per output
-// element and 32-wide block).  Every operand a wave needs is staged in LDS one
+// The fp32 rescale (1.5 FMAs per output element and 32-wide block, the
+// three-FMA magic-number form) costs three times the MFMA issue time, so the
+// kernel is VALU-bound and keeps every other VALU op out of the inner loop:
+// the nibble -> int8 unpack and the weight-scale preparation are done once
+// per workgroup into LDS.  Every operand a wave needs is staged in LDS one
 // chunk ahead (double buffer), so a wave only waits on LDS, and two
 // workgroups fit on a CU.
 constexpr int kTM = 128;          // workgroup tile rows (tokens)
