@@ -28,6 +28,7 @@
 
 #include "q4w_internal.h"
 #include <hip/hip_fp16.h>
+#include <cstddef>
 
 namespace q4w {
 namespace {
@@ -324,9 +325,20 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   stage_commit(lds[0]);
   __syncthreads();
 
+  // Per-lane LDS byte offsets inside a chunk buffer; every operand read of
+  // the unrolled group loop below is one of these plus a compile-time offset.
+  const int off_a = (int)offsetof(ChunkLds, aq) + ((wm * 2 * kChunkBlocks) * 64 + lane) * 16;
+  int off_b[kChunkBlocks];
+#pragma unroll
+  for (int bl = 0; bl < kChunkBlocks; ++bl)
+    off_b[bl] = (int)offsetof(ChunkLds, bq) + ((wn * 2 * kChunkBlocks) * 64 + (lane ^ (4 * bl))) * 16;
+  const int off_sd = (int)offsetof(ChunkLds, sd) + (wn * 64 + j) * 4;
+  const int off_sb = (int)offsetof(ChunkLds, sb) + (wn * 64 + j) * 4;
+  const int off_sa = (int)offsetof(ChunkLds, sa) + (wm * 64 + 4 * h) * 4;
+
 #pragma unroll 1
   for (int c = 0; c < nchunks; ++c) {
-    const ChunkLds& L = lds[c & 1];
+    const char* L = reinterpret_cast<const char*>(&lds[c & 1]);
     stage_issue(c + 1);                       // out of range past the last chunk
 #pragma unroll
     for (int gi = 0; gi < kChunkGroups; ++gi) {
@@ -337,16 +349,17 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
         float sav[2][16];
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) {
-          const int ms = wm * 2 + mi;
 #pragma unroll
           for (int bi = 0; bi < 2; ++bi) {
-            const uint4 t = L.aq[(ms * kChunkBlocks + bl0 + bi) * 64 + lane];
+            const uint4 t = *reinterpret_cast<const uint4*>(
+                L + off_a + ((mi * kChunkBlocks + bl0 + bi) * 64) * 16);
             av[mi][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
           }
           if (!kDebug) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float4 f = *reinterpret_cast<const float4*>(&L.sa[gi * kTM + ms * 32 + 8 * r + 4 * h]);
+              const float4 f = *reinterpret_cast<const float4*>(
+                  L + off_sa + (gi * kTM + mi * 32 + 8 * r) * 4);
               sav[mi][4 * r + 0] = f.x; sav[mi][4 * r + 1] = f.y;
               sav[mi][4 * r + 2] = f.z; sav[mi][4 * r + 3] = f.w;
             }
@@ -354,17 +367,18 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
         }
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          const int ns = wn * 2 + ni;
-          const int col = ns * 32 + j;
-          const uint4 b0r = L.bq[(ns * kChunkBlocks + bl0) * 64 + (lane ^ (4 * bl0))];
-          const uint4 b1r = L.bq[(ns * kChunkBlocks + bl0 + 1) * 64 + (lane ^ (4 * (bl0 + 1)))];
+          const int col = (wn * 2 + ni) * 32 + j;
+          const uint4 b0r = *reinterpret_cast<const uint4*>(
+              L + off_b[bl0] + ((ni * kChunkBlocks + bl0) * 64) * 16);
+          const uint4 b1r = *reinterpret_cast<const uint4*>(
+              L + off_b[bl0 + 1] + ((ni * kChunkBlocks + bl0 + 1) * 64) * 16);
           const v4i bv0 = v4i{(int)b0r.x, (int)b0r.y, (int)b0r.z, (int)b0r.w};
           const v4i bv1 = v4i{(int)b1r.x, (int)b1r.y, (int)b1r.z, (int)b1r.w};
           float d0 = 0.f, d1 = 0.f, nc = 0.f;
           if (!kDebug) {
-            d0 = L.sd[bl0 * kSdStride + col];
-            d1 = L.sd[(bl0 + 1) * kSdStride + col];
-            nc = L.sb[gi * kTN + col];
+            d0 = *reinterpret_cast<const float*>(L + off_sd + (bl0 * kSdStride + ni * 32) * 4);
+            d1 = *reinterpret_cast<const float*>(L + off_sd + ((bl0 + 1) * kSdStride + ni * 32) * 4);
+            nc = *reinterpret_cast<const float*>(L + off_sb + (gi * kTN + ni * 32) * 4);
           }
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {

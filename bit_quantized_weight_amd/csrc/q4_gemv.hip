@@ -82,7 +82,7 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 // Rows per lane: more rows re-use the activation registers more (less LDS
 // traffic per weight) at the cost of registers and of fewer workgroups.
 // (This kernel serves M = 1..3; wider M goes to the matrix-core kernel.)
-__host__ __device__ constexpr int rows_per_lane(int M) { return M == 1 ? 1 : 2; }
+__host__ __device__ constexpr int rows_per_lane(int) { return 2; }
 // Steps requested at once per wave (the register ring).
 __host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : 4; }
 // Occupancy target (waves per SIMD).
