@@ -137,7 +137,7 @@ def bench_verify(torch, q4w, synthetic, steps, warmup):
     k, n = wl["K"], wl["N"]
     copies = make_copies(torch, q4w, synthetic, n, k, 20_000)
     res = {}
-    for m in (1, 2, 3, 4, 5):
+    for m in (1, 2, 3, 4, 5, 8, 13, 16):      # 1..5: the verify workload; 8..16: wide drafts
         x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
         tg, te = gemv_series(torch, q4w, copies, x, y, steps, warmup)

@@ -154,7 +154,7 @@ def q4_gemv_skinny_raw(x, codes, scales, y, split_k=0, ws=None):
 
 
 def gemv(x, codes, scales, split_k=0):
-    """fp16 X [M<=8, K] against packed weights -> fp16 Y [M, N]."""
+    """fp16 X [M<=16, K] against packed weights -> fp16 Y [M, N]."""
     import torch
     _need(x, torch.float16, "x")
     _need(codes, torch.uint8, "codes")

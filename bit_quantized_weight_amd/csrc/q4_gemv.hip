@@ -1,4 +1,4 @@
-// q4_gemv_skinny: Y[M, N] = X[M, K] . What^T for M <= 8 -- the weight stream
+// q4_gemv_skinny: Y[M, N] = X[M, K] . What^T for small M -- the weight stream
 // of autoregressive decode and of speculative verification.
 //
 // Pages: decode streams every quantized weight once per step and is bound by

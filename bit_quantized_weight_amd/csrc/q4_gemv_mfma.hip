@@ -1,4 +1,4 @@
-// q4_gemv_skinny on the matrix cores, for the verify widths 4 <= M <= 8.
+// q4_gemv_skinny on the matrix cores, for the verify widths 4 <= M <= 16.
 //
 // The VALU form of the skinny matmul pays M/2 dot2 lane-ops per weight, which
 // outgrows the HBM stream as M grows (speculative verification scores
@@ -59,6 +59,12 @@ constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks
 // not stored: their lanes read a shared zero octet instead.
 __host__ __device__ constexpr int mp4(int M) { return (M + 3) / 4 * 4; }
 __host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * mp4(M); }
+// Steps of one slice: at most kMaxSliceSteps, and few enough that the
+// slice's (block, row) staging items fit one per thread.
+__host__ __device__ constexpr int max_slice_steps(int M) {
+  return kThreads / (kBlocksPerStep * mp4(M)) < kMaxSliceSteps ? kThreads / (kBlocksPerStep * mp4(M))
+                                                               : kMaxSliceSteps;
+}
 constexpr int kLdsZeroBytes = 32;            // one zero octet + one zero float4
 __host__ __device__ constexpr int lds_bytes(int M, int bpad) {
   return bpad * lds_bytes_per_block(M) + kLdsZeroBytes;
@@ -182,7 +188,7 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, 0, M * K * 2, kRsrcWord3);
   // One (block, row) item per thread: bpad x Mp4 <= 32 x 8 items.
-  static_assert(kMaxSliceSteps * kBlocksPerStep * mp4(8) <= kThreads, "one staging item per thread");
+  static_assert(max_slice_steps(M) * kBlocksPerStep * mp4(M) <= kThreads, "one staging item per thread");
   constexpr int MP = mp4(M);
   const int sb = tid / MP;                 // staging block
   const int sm = tid % MP;                 // staging row
@@ -354,7 +360,9 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
 // Two LDS activation buffers alternate by chunk.
 // Steps per chunk of the streaming kernel (two chunks of loads stay in
 // registers) and 64-row tiles per work item.
-__host__ __device__ constexpr int stream_steps(bool quad) { return quad ? STREAM_P : 4; }
+__host__ __device__ constexpr int stream_steps(int M, bool quad) {
+  return !quad ? 4 : (max_slice_steps(M) / 4 * 4 < STREAM_P ? max_slice_steps(M) / 4 * 4 : STREAM_P);
+}
 constexpr int kStreamTiles = STREAM_TILES;
 
 struct Walker {
@@ -369,7 +377,7 @@ struct Walker {
 template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(STREAM_WAVES, 8)))
 mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_items) {
-  constexpr int P = stream_steps(kScaleQuad);
+  constexpr int P = stream_steps(M, kScaleQuad);
   constexpr int T = kStreamTiles;
   constexpr int kChunkBlocks = P * kBlocksPerStep;
   constexpr int MP = mp4(M);
@@ -663,7 +671,7 @@ SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
   const int nb = (int)(K / kBlock);
   const int steps_total = (nb + kBlocksPerStep - 1) / kBlocksPerStep;
   static_assert(kMaxSliceSteps <= mfma_ring_steps(0), "a slice fits the ring");
-  const int lds_steps = kMaxSliceSteps;
+  const int lds_steps = max_slice_steps(M);
   int steps;
   if (split_k > 0) {
     steps = (steps_total + split_k - 1) / split_k;
@@ -727,7 +735,7 @@ const void* batched_kernel_ptr(bool quad) {
 }
 
 // LDS of the streaming kernel: two chunk buffers.
-int batched_lds(int M, bool quad) { return 2 * lds_bytes(M, stream_steps(quad) * kBlocksPerStep); }
+int batched_lds(int M, bool quad) { return 2 * lds_bytes(M, stream_steps(M, quad) * kBlocksPerStep); }
 
 const void* batched_kernel_for(int M, bool quad) {
   switch (M) {
@@ -739,6 +747,14 @@ const void* batched_kernel_for(int M, bool quad) {
     case 6: return batched_kernel_ptr<6>(quad);
     case 7: return batched_kernel_ptr<7>(quad);
     case 8: return batched_kernel_ptr<8>(quad);
+    case 9: return batched_kernel_ptr<9>(quad);
+    case 10: return batched_kernel_ptr<10>(quad);
+    case 11: return batched_kernel_ptr<11>(quad);
+    case 12: return batched_kernel_ptr<12>(quad);
+    case 13: return batched_kernel_ptr<13>(quad);
+    case 14: return batched_kernel_ptr<14>(quad);
+    case 15: return batched_kernel_ptr<15>(quad);
+    case 16: return batched_kernel_ptr<16>(quad);
     default: return nullptr;
   }
 }
@@ -780,6 +796,14 @@ hipError_t launch_skinny_mfma(const uint16_t* x, const uint8_t* codes, const uin
     case 6: return launch_mfma_m<6>(x, codes, scales, y, N, K, p, ws, s);
     case 7: return launch_mfma_m<7>(x, codes, scales, y, N, K, p, ws, s);
     case 8: return launch_mfma_m<8>(x, codes, scales, y, N, K, p, ws, s);
+    case 9: return launch_mfma_m<9>(x, codes, scales, y, N, K, p, ws, s);
+    case 10: return launch_mfma_m<10>(x, codes, scales, y, N, K, p, ws, s);
+    case 11: return launch_mfma_m<11>(x, codes, scales, y, N, K, p, ws, s);
+    case 12: return launch_mfma_m<12>(x, codes, scales, y, N, K, p, ws, s);
+    case 13: return launch_mfma_m<13>(x, codes, scales, y, N, K, p, ws, s);
+    case 14: return launch_mfma_m<14>(x, codes, scales, y, N, K, p, ws, s);
+    case 15: return launch_mfma_m<15>(x, codes, scales, y, N, K, p, ws, s);
+    case 16: return launch_mfma_m<16>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

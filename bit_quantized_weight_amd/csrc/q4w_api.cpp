@@ -30,7 +30,7 @@ constexpr int kMaxBatch = 1 << 20;
 // Sizes and shapes of a batch (pointers are not looked at).
 int check_batch_shapes(int M, const q4w_gemv_desc* d, int count) {
   if (!d || count < 1 || count > kMaxBatch) return Q4W_ERR_INVALID_ARG;
-  if (M < 1 || M > 8) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M < 1 || M > q4w::kMaxSkinnyM) return Q4W_ERR_UNSUPPORTED_SHAPE;
   for (int g = 0; g < count; ++g) {
     if (d[g].N <= 0 || d[g].K <= 0) return Q4W_ERR_INVALID_ARG;
     if (d[g].K % q4w::kBlock != 0 || d[g].N > q4w::kMaxSkinnyN || d[g].K > kMaxSkinnyK)
@@ -65,7 +65,7 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
 }
 
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k) {
-  if (M < 1 || M > 8 || N <= 0 || N > q4w::kMaxSkinnyN || K <= 0 || K > kMaxSkinnyK ||
+  if (M < 1 || M > q4w::kMaxSkinnyM || N <= 0 || N > q4w::kMaxSkinnyN || K <= 0 || K > kMaxSkinnyK ||
       K % q4w::kBlock != 0 || split_k < 0 || split_k > 64)
     return 0;
   return q4w::plan_skinny(M, N, K, split_k).ws_bytes;
@@ -75,7 +75,7 @@ int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scal
                    int M, int64_t N, int64_t K, int split_k, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
   if (N < 0 || K < 0 || split_k < 0 || split_k > 64) return Q4W_ERR_INVALID_ARG;
-  if (M < 1 || M > 8 || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M < 1 || M > q4w::kMaxSkinnyM || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (N > q4w::kMaxSkinnyN || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (N == 0) return Q4W_OK;
   if (!y) return Q4W_ERR_INVALID_ARG;
@@ -240,7 +240,7 @@ int q4_gemv_batched_plan(int M, const q4w_gemv_desc* descs, int count, void* ws,
 }
 
 int q4_gemv_batched_run(const q4w_batched_plan* plan, hipStream_t stream) {
-  if (!plan || !plan->ws || plan->M < 1 || plan->M > 8 || plan->count < 1 ||
+  if (!plan || !plan->ws || plan->M < 1 || plan->M > q4w::kMaxSkinnyM || plan->count < 1 ||
       plan->total_items < 1 || plan->grid < 1 || plan->variant < 0 || plan->variant > 1)
     return Q4W_ERR_INVALID_ARG;
   return hip_status(q4w::launch_batched(plan->M, plan->variant == 1, plan->ws, plan->count,

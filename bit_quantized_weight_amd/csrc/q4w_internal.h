@@ -16,7 +16,8 @@ constexpr int kActGroup = 64;     // activation channels per int8 scale (A8 rout
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, uint8_t* codes,
                        uint16_t* scales, hipStream_t s);
 
-// ---- skinny (M <= 8) weight-streaming matmul ------------------------------
+// ---- skinny (M <= 16) weight-streaming matmul -----------------------------
+constexpr int kMaxSkinnyM = 16;
 // Split-K arrival counters: one uint32 per row tile, in a fixed region at the
 // start of the workspace.  The smallest row tile is 8 rows, so 65536 counters
 // cover N <= 2^19.

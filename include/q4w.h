@@ -73,7 +73,10 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
             hipStream_t stream);
 
 /*
- * q4_gemv_skinny: Y[M, N] = X[M, K] . What^T for 1 <= M <= 8 (decode, verify).
+ * q4_gemv_skinny: Y[M, N] = X[M, K] . What^T for 1 <= M <= 16 (decode, and
+ *   verification of up to 15 drafted tokens: the 12-token DFlash2 draft
+ *   window of page 5, section "DFlash2 reached 282 tok/s on a code prompt",
+ *   verifies M = 13 rows).
  *   x      [M, K] fp16, 16-byte aligned.      y [M, N] fp16 (RNE of an fp32
  *   accumulation), 4-byte aligned.            codes/scales as above.
  *   split_k: 0 = library choice, else 1..64 slices of K reduced in a fixed
@@ -84,7 +87,7 @@ int q4_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scal
  *   fp32 partial sums.  The workspace must be zero-filled once before its
  *   first use; every completed call leaves the counter region zeroed again,
  *   so one workspace may serve any sequence of shapes (not concurrently).
- *   M outside [1, 8], K % 32 != 0, K > 2^24 or N > 2^19: UNSUPPORTED_SHAPE.
+ *   M outside [1, 16], K % 32 != 0, K > 2^24 or N > 2^19: UNSUPPORTED_SHAPE.
  *   N == 0: OK, nothing enqueued.  K == 0: y is filled with zeros.
  */
 size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
@@ -150,7 +153,7 @@ int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
 
 /*
  * Batched skinny matmuls: one persistent launch computes a whole list of
- * independent y_g = x_g . What_g^T (same M for all, 1 <= M <= 8), e.g. every
+ * independent y_g = x_g . What_g^T (same M for all, 1 <= M <= 16), e.g. every
  * projection of every layer of one decode step, which the pages' decode
  * streams once per token ("Qwen3.8-27B at 256K on a 24GB RTX PRO 4000 SFF",
  * page 3, the paragraph on weight streaming during decode).  Work items of

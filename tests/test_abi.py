@@ -74,7 +74,7 @@ def test_pack_checks(L):
 def test_gemv_checks(L):
     g = L.q4_gemv_skinny
     assert g(p(A), p(A), p(A), p(A), 0, 64, 64, 0, NUL, 0, NUL) == SHAPE    # M < 1
-    assert g(p(A), p(A), p(A), p(A), 9, 64, 64, 0, NUL, 0, NUL) == SHAPE    # M > 8
+    assert g(p(A), p(A), p(A), p(A), 17, 64, 64, 0, NUL, 0, NUL) == SHAPE   # M > 16
     assert g(p(A), p(A), p(A), p(A), 1, 64, 48, 0, NUL, 0, NUL) == SHAPE    # K % 32
     assert g(p(A), p(A), p(A), p(A), 1, 64, (1 << 24) + 32, 0, NUL, 0, NUL) == SHAPE
     assert g(p(A), p(A), p(A), p(A), 1, -1, 64, 0, NUL, 0, NUL) == INVALID
@@ -96,7 +96,8 @@ def test_gemv_checks(L):
 
 def test_gemv_ws_sizes(L):
     f = L.q4_gemv_skinny_ws_bytes
-    assert f(0, 64, 64, 0) == 0 and f(9, 64, 64, 0) == 0 and f(1, 64, 48, 0) == 0
+    assert f(0, 64, 64, 0) == 0 and f(17, 64, 64, 0) == 0 and f(1, 64, 48, 0) == 0
+    assert f(16, 5120, 17408, 0) > 0               # verify widths up to 16
     assert f(1, 512, 256, 1) == 0                  # one slice: no partials
     # explicit split: S slices x M x N fp32 partials plus the counter region
     s = f(2, 1000, 1024, 4)
@@ -169,7 +170,8 @@ def test_batched_checks(L):
     pl = ctypes.byref(plan)
     one = _descs([good])
     assert ws_bytes(5, one, 1) > 0
-    assert ws_bytes(5, one, 0) == 0 and ws_bytes(0, one, 1) == 0 and ws_bytes(9, one, 1) == 0
+    assert ws_bytes(5, one, 0) == 0 and ws_bytes(0, one, 1) == 0 and ws_bytes(17, one, 1) == 0
+    assert ws_bytes(16, one, 1) > 0
     assert ws_bytes(5, None, 1) == 0
     assert ws_bytes(5, _descs([(A, A, A, A, 64, 48)]), 1) == 0       # K % 32
     assert ws_bytes(5, _descs([(A, A, A, A, 0, 64)]), 1) == 0        # N == 0
@@ -182,7 +184,7 @@ def test_batched_checks(L):
     assert bp(5, None, 1, p(A), need, pl) == INVALID
     assert bp(5, one, 0, p(A), need, pl) == INVALID
     assert bp(0, one, 1, p(A), need, pl) == SHAPE
-    assert bp(9, one, 1, p(A), need, pl) == SHAPE
+    assert bp(17, one, 1, p(A), need, pl) == SHAPE
     assert bp(5, _descs([(A, A, A, A, -1, 64)]), 1, p(A), need, pl) == INVALID
     assert bp(5, _descs([(A, A, A, A, 64, 0)]), 1, p(A), need, pl) == INVALID
     assert bp(5, _descs([(A, A, A, A, 64, 96 + 16)]), 1, p(A), need, pl) == SHAPE

@@ -209,7 +209,7 @@ def test_large_n_split_counters(m):
 BATCH_SHAPES = [(100, 96), (300, 1056), (257, 5120), (70, 8192), (5120, 17408), (64, 512)]
 
 
-@pytest.mark.parametrize("m", [1, 3, 4, 5, 8])
+@pytest.mark.parametrize("m", [1, 3, 4, 5, 8, 13, 16])
 def test_batched_matches_oracle_and_repeats(m):
     """One persistent launch over six matmuls of mixed, ragged shapes (K not
     a multiple of 128 included): each output within the bar of the oracle,
@@ -260,3 +260,39 @@ def test_batched_aligned_and_ragged_k_variants():
         torch.cuda.synchronize()
         for (n, k), it, ref in zip(shapes, items, refs):
             assert_close(host(it[3]), ref, what=f"variant test N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [9, 12, 13, 16])
+@pytest.mark.parametrize("n,k", [(100, 96), (300, 1056), (257, 5120), (70, 8192)])
+def test_wide_verify_shapes(m, n, k):
+    """Verify widths 9..16 (a 12-token draft window verifies 13 rows) on
+    ragged shapes: N not a multiple of the 64-row tile, K not a multiple of
+    the slice."""
+    codes, scales, q, d = packed(n, k, 10 + n)
+    x = synthetic.activations(m, k, 20 + m)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what=f"M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [8, 13, 16])
+def test_verify_down_wide(m):
+    """Speculative verify, down-projection shape, at M = 8, 13, 16."""
+    w = synthetic.WORKLOADS["verify_down"]
+    codes, scales, q, d = packed(w["N"], w["K"], synthetic.WEIGHT_SEED)
+    x = synthetic.activations(m, w["K"], synthetic.ACT_SEED)
+    assert_close(run(x, codes, scales), q4.matmul(x, q, d), what=f"verify_down M={m}")
+
+
+def test_one_hot_bit_exact_wide():
+    """One-hot rows through the 16-row matrix-core path: every output is one
+    product rounded once, so the result is bit-exact."""
+    n, k = 96, 256
+    codes, scales, q, d = packed(n, k, 41)
+    for start in (0, 16, 240):
+        x = np.zeros((16, k), np.float16)
+        for r in range(16):
+            x[r, start + r] = 1.0
+        y = run(x, codes, scales)
+        for r in range(16):
+            kk = start + r
+            want = (q[:, kk].astype(np.float64) * d[:, kk // 32].astype(np.float64)).astype(np.float16)
+            assert np.array_equal(y[r], want), kk
