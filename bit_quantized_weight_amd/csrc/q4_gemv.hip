@@ -45,6 +45,7 @@ namespace {
 
 constexpr int kWaves = 4;               // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr int kFixupBatch = 16;         // split-K fixup: partial loads in flight per thread
 constexpr int kLanesPerRow = 32;        // lanes sharing one row along K
 constexpr int kSlots = 64 / kLanesPerRow;
 constexpr int kLdsBudget = 48 * 1024;   // activation staging bytes per workgroup
@@ -322,14 +323,7 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   }
   __syncthreads();
   if (!is_last) return;
-  for (int o = tid; o < kRowsPerWg * M; o += kThreads) {
-    const int m = o / kRowsPerWg;
-    const int n = tile_row0 + (o - m * kRowsPerWg);
-    if (n < N) {
-      const float s = sum_partials(&partial[(size_t)m * N + n], (size_t)M * N, S);
-      y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(s));
-    }
-  }
+  fixup_tile<kRowsPerWg, M, kThreads, kFixupBatch>(partial, y, N, S, tile_row0);
   if (tid == 0)   // leave the workspace ready for the next call
     __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

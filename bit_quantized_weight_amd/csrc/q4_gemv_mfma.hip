@@ -49,6 +49,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// Split-K fixup: partial loads in flight per thread.  A 64-row tile at M <= 8
+// has at most 2 outputs per thread, so S <= 18 slices take one round.
+constexpr int kFixupBatch = 36;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kBlocksPerStep = 4;            // one 128-bit load per lane = 4 blocks per lane group set
@@ -325,20 +328,18 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   }
   __syncthreads();
   if (!is_last) return;
-  for (int o = tid; o < kRowsPerWg * M; o += kThreads) {
-    const int m = o / kRowsPerWg;
-    const int n = tile_row0 + (o - m * kRowsPerWg);
-    if (n < N) {
-      const float s = sum_partials(&partial[(size_t)m * N + n], (size_t)M * N, S);
-      y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(s));
-    }
-  }
+  fixup_tile<kRowsPerWg, M, kThreads, kFixupBatch>(partial, y, N, S, tile_row0);
   if (tid == 0)
     __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Occupancy floor: with 6 waves per SIMD (at most 80 VGPRs) every workgroup
+// of a 1024..1536-workgroup split plan is resident at once, so no second
+// partial wave of workgroups trails the stream.  The four-load scale form
+// needs more registers and takes what fits without spilling.
 template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kScaleQuad ? 6 : (M == 4 ? 4 : 5), 8)))
 mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
                    const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
                    float* __restrict__ partial, uint32_t* __restrict__ counters,
