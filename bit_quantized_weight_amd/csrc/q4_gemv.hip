@@ -49,6 +49,7 @@ constexpr int kFixupBatch = 16;         // split-K fixup: partial loads in fligh
 constexpr int kLanesPerRow = 32;        // lanes sharing one row along K
 constexpr int kSlots = 64 / kLanesPerRow;
 constexpr int kLdsBudget = 48 * 1024;   // activation staging bytes per workgroup
+constexpr int kMinSkinnyWgs = 256;      // one workgroup per CU
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -358,11 +359,10 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
 
 }  // namespace
 
-// Split plan.  A slice is a whole number of 32-block steps; the number of
-// slices S is chosen so that (a) a slice's activations fit the LDS budget,
-// (b) a slice is at most two rings long, and (c) there are enough
-// workgroups to fill the GPU.  split_k > 0 asks for that many slices (raised
-// when the LDS budget needs more).
+// Split plan.  A slice is a whole number of 32-block steps and its
+// activations fit the LDS budget (at most two rings long); S is as small as
+// the rules below allow.  split_k > 0 asks for that many slices (raised when
+// the LDS budget needs more).
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   if (M >= kMfmaMinM) return plan_skinny_mfma(M, N, K, split_k);
   SkinnyPlan p{};
@@ -376,12 +376,17 @@ SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
     bps = (nb + split_k - 1) / split_k;
     if (bps > lds_blocks) bps = lds_blocks;
   } else {
+    // Split-K ends the launch with a chain of memory round trips (partial
+    // stores, the arrival count, the last workgroup's partial loads).  On the
+    // measured shapes that chain costs more than one ring refill, and more
+    // than running with as few as one workgroup per CU, so: one slice when
+    // the row fits two rings, else the fewest slices that need no refill;
+    // more slices only below kMinSkinnyWgs workgroups.
     const int steps_total = (nb + kLanesPerRow - 1) / kLanesPerRow;
-    int max_steps = lds_blocks / kLanesPerRow;
-    if (max_steps < 1) max_steps = 1;
-    int S = (steps_total + max_steps - 1) / max_steps;
-    const int target_wgs = 1024;   // about four workgroups per CU on 256 CUs
-    while ((int64_t)S * p.row_tiles < target_wgs && steps_total / (S + 1) >= 2) ++S;
+    const int max_steps = lds_blocks / kLanesPerRow;            // two rings, or the LDS budget
+    const int ring = ring_steps(M);
+    int S = steps_total <= max_steps ? 1 : (steps_total + ring - 1) / ring;
+    while ((int64_t)S * p.row_tiles < kMinSkinnyWgs && steps_total / (S + 1) >= 1) ++S;
     bps = ((steps_total + S - 1) / S) * kLanesPerRow;
   }
   if (bps < 1) bps = 1;
