@@ -105,6 +105,35 @@ def test_gemv_ws_sizes(L):
     assert s % 256 == 0 or s > 0
 
 
+def test_gemv_split_policy(L):
+    """The library's split choice, read through the workspace size (the 256 KiB
+    counter region plus S x M x N fp32 partials, none when S = 1)."""
+    f = L.q4_gemv_skinny_ws_bytes
+    region = 256 * 1024
+
+    def slices(m, n, k):
+        b = f(m, n, k, 0)
+        if b == 0:
+            return 1
+        assert (b - region) % (m * n * 4) == 0, (m, n, k, b)
+        return (b - region) // (m * n * 4)
+
+    # VALU kernel (M <= 3): one slice when a row fits two register rings ...
+    assert slices(1, 17408, 5120) == 1        # decode gate/up
+    assert slices(1, 7168, 5120) == 1         # qkv
+    assert slices(1, 5120, 5120) == 1         # out
+    assert slices(2, 17408, 5120) == 1
+    # ... else the fewest slices that need no ring refill (6 steps at M = 1, 4 above)
+    assert slices(1, 5120, 17408) == 3        # verify down: 17 steps of 32 blocks
+    assert slices(2, 5120, 17408) == 5
+    assert slices(3, 5120, 17408) == 5
+    # ... and more slices only below 256 workgroups (16 rows each)
+    assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
+    # matrix-core kernel (M >= 4): slices of at most 8 steps of 4 blocks
+    assert slices(4, 5120, 17408) == 17
+    assert slices(5, 5120, 17408) == 17
+
+
 def test_act_quant_checks(L):
     q = L.a8_quantize_act
     assert q(p(A), -1, 64, p(A), p(A), NUL) == INVALID
