@@ -62,11 +62,17 @@ constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks
 // not stored: their lanes read a shared zero octet instead.
 __host__ __device__ constexpr int mp4(int M) { return (M + 3) / 4 * 4; }
 __host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * mp4(M); }
-// Steps of one slice: at most kMaxSliceSteps, and few enough that the
-// slice's (block, row) staging items fit one per thread.
-__host__ __device__ constexpr int max_slice_steps(int M) {
-  return kThreads / (kBlocksPerStep * mp4(M)) < kMaxSliceSteps ? kThreads / (kBlocksPerStep * mp4(M))
-                                                               : kMaxSliceSteps;
+// Steps of a K-chunk whose (block, row) staging items fit kItems per thread,
+// at most kMaxSliceSteps.  The streaming kernel stages one item per thread;
+// the single-launch kernel up to two (8 steps for every M <= 16).
+__host__ __device__ constexpr int chunk_steps(int M, int items) {
+  return items * kThreads / (kBlocksPerStep * mp4(M)) < kMaxSliceSteps
+             ? items * kThreads / (kBlocksPerStep * mp4(M))
+             : kMaxSliceSteps;
+}
+__host__ __device__ constexpr int max_slice_steps(int M) { return chunk_steps(M, 2); }
+__host__ __device__ constexpr int stage_items(int M) {
+  return (max_slice_steps(M) * kBlocksPerStep * mp4(M) + kThreads - 1) / kThreads;
 }
 constexpr int kLdsZeroBytes = 32;            // one zero octet + one zero float4
 __host__ __device__ constexpr int lds_bytes(int M, int bpad) {
@@ -190,19 +196,22 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   // past the slice read zeros (out-of-range offset, no memory request).
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, 0, M * K * 2, kRsrcWord3);
-  // One (block, row) item per thread: bpad x Mp4 <= 32 x 8 items.
-  static_assert(max_slice_steps(M) * kBlocksPerStep * mp4(M) <= kThreads, "one staging item per thread");
+  // Item u = tid + it * kThreads is (block u / Mp4, row u % Mp4):
+  // bpad x Mp4 <= kItems x kThreads items (one per thread up to M = 8).
   constexpr int MP = mp4(M);
-  const int sb = tid / MP;                 // staging block
-  const int sm = tid % MP;                 // staging row
-  uint4 raw[4];
-  {
+  constexpr int kItems = stage_items(M);
+  static_assert(max_slice_steps(M) * kBlocksPerStep * MP <= kItems * kThreads, "staging items");
+  uint4 raw[kItems][4];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int u = tid + it * kThreads;
+    const int sb = u / MP, sm = u % MP;
     const bool valid = sm < M && sb < nbs;
     const uint32_t xo = valid ? (uint32_t)(sm * K + (kb0 + sb) * kBlock) * 2 : kOutOfRange;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, q * 16, 0);
-      raw[q] = make_uint4(v[0], v[1], v[2], v[3]);
+      raw[it][q] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
 
@@ -217,24 +226,29 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   const int zero_off = bpad * lds_bytes_per_block(M);                  // zero octet, zero float4
   const uint32_t k1032 = 0x64086408u;
   const uint32_t k72 = 0x54805480u;
-  if (sb < bpad) {
-    float c = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
-      const uint32_t w0 = raw[q].x, w1 = raw[q].y, w2 = raw[q].z, w3 = raw[q].w;
-      uint4 o;
-      o.x = (w0 & 0xFFFFu) | (w2 << 16);
-      o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
-      o.z = (w1 & 0xFFFFu) | (w3 << 16);
-      o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
-      if (sm < M) xs[(sb * 4 + q) * M + sm] = o;
-      c = dot2(o.x, k1032, c);
-      c = dot2(o.y, k72, c);
-      c = dot2(o.z, k1032, c);
-      c = dot2(o.w, k72, c);
+  for (int it = 0; it < kItems; ++it) {
+    const int u = tid + it * kThreads;
+    const int sb = u / MP, sm = u % MP;
+    if (sb < bpad) {
+      float c = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // elements e0..e7 of code word q -> (e0,e4), (e1,e5), (e2,e6), (e3,e7)
+        const uint32_t w0 = raw[it][q].x, w1 = raw[it][q].y, w2 = raw[it][q].z, w3 = raw[it][q].w;
+        uint4 o;
+        o.x = (w0 & 0xFFFFu) | (w2 << 16);
+        o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);
+        o.z = (w1 & 0xFFFFu) | (w3 << 16);
+        o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);
+        if (sm < M) xs[(sb * 4 + q) * M + sm] = o;
+        c = dot2(o.x, k1032, c);
+        c = dot2(o.y, k72, c);
+        c = dot2(o.z, k1032, c);
+        c = dot2(o.w, k72, c);
+      }
+      cl[sb * MP + sm] = -c;               // rows >= M read zeros, so c == 0 there
     }
-    cl[sb * MP + sm] = -c;                 // rows >= M read zeros, so c == 0 there
   }
   if (tid < 2) reinterpret_cast<uint4*>(lds + zero_off)[tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
@@ -335,11 +349,12 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
 
 // Occupancy floor: with 6 waves per SIMD (at most 80 VGPRs) every workgroup
 // of a 1024..1536-workgroup split plan is resident at once, so no second
-// partial wave of workgroups trails the stream.  The four-load scale form
-// needs more registers and takes what fits without spilling.
+// partial wave of workgroups trails the stream.  Two staging items per
+// thread (M > 8) and the four-load scale form need more registers and take
+// what fits without spilling.
 template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kScaleQuad ? 6 : (M == 4 ? 4 : 5), 8)))
+__attribute__((amdgpu_waves_per_eu(kScaleQuad ? (stage_items(M) > 1 ? 5 : 6) : (M == 4 || stage_items(M) > 1 ? 4 : 5), 8)))
 mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
                    const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
                    float* __restrict__ partial, uint32_t* __restrict__ counters,
@@ -362,7 +377,7 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
 // Steps per chunk of the streaming kernel (two chunks of loads stay in
 // registers) and 64-row tiles per work item.
 __host__ __device__ constexpr int stream_steps(int M, bool quad) {
-  return !quad ? 4 : (max_slice_steps(M) / 4 * 4 < STREAM_P ? max_slice_steps(M) / 4 * 4 : STREAM_P);
+  return !quad ? 4 : (chunk_steps(M, 1) / 4 * 4 < STREAM_P ? chunk_steps(M, 1) / 4 * 4 : STREAM_P);
 }
 constexpr int kStreamTiles = STREAM_TILES;
 

@@ -129,9 +129,10 @@ def test_gemv_split_policy(L):
     assert slices(3, 5120, 17408) == 5
     # ... and more slices only below 256 workgroups (16 rows each)
     assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
-    # matrix-core kernel (M >= 4): slices of at most 8 steps of 4 blocks
-    assert slices(4, 5120, 17408) == 17
-    assert slices(5, 5120, 17408) == 17
+    # matrix-core kernel (M >= 4): slices of at most 8 steps of 4 blocks, at
+    # every width up to 16 (two activation staging items per thread past M = 8)
+    for m in (4, 5, 8, 9, 13, 16):
+        assert slices(m, 5120, 17408) == 17, m
 
 
 def test_act_quant_checks(L):
