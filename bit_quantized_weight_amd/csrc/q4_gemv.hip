@@ -50,6 +50,7 @@ constexpr int kLanesPerRow = 32;        // lanes sharing one row along K
 constexpr int kSlots = 64 / kLanesPerRow;
 constexpr int kLdsBudget = 48 * 1024;   // activation staging bytes per workgroup
 constexpr int kMinSkinnyWgs = 256;      // one workgroup per CU
+constexpr int kCachePolicyNT = 2;       // buffer-load cache policy bit: non-temporal (streaming)
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -153,7 +154,11 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
     for (int i = 0; i < RL; ++i) {
       const uint32_t vo = live ? vblk[i] * kBlockBytes : kOutOfRange;
       const uint32_t so = live ? vblk[i] * 2 : kOutOfRange;
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kLanesPerRow * kBlockBytes, 0);
+      // Non-temporal: every code byte is read once, as whole 128-byte lines
+      // (a wave reads 2 rows x 512 B), so nothing is gained by keeping it in
+      // the caches.  (The scales are read in half lines, which the next step
+      // completes from L2, so they keep the default policy.)
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kLanesPerRow * kBlockBytes, kCachePolicyNT);
       c[i] = make_uint4(v[0], v[1], v[2], v[3]);
       sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kLanesPerRow * 2, 0);
     }
