@@ -32,6 +32,12 @@
 #include "splitk.h"
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <utility>
+#include <vector>
+
 // Streaming kernel shape (measured best on the 64-layer decode step at M = 1
 // and 5): 8-step chunks, 3 waves per SIMD, 4 row tiles per work item.
 #ifndef STREAM_P
@@ -367,7 +373,8 @@ mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ cod
 // Streaming form: one persistent launch computes every matmul of a table
 // (same M).  A work item is kStreamTiles row tiles of 64 rows over the whole
 // of K (no split-K: no partials, no arrival counters, no waits on store
-// completion).  A workgroup walks items w, w + gridDim.x, ... as a sequence
+// completion).  A workgroup walks its own list of items (dealt at plan time
+// so that every workgroup gets about the same rows x K) as a sequence
 // of units (K-chunk c, tile t), tile innermost: the activations of chunk c
 // are staged into LDS once (one barrier) and serve all tiles of the item.
 // The loads of the next unit (codes, scales, and activations at tile 0) go
@@ -382,6 +389,8 @@ __host__ __device__ constexpr int stream_steps(int M, bool quad) {
 constexpr int kStreamTiles = STREAM_TILES;
 
 struct Walker {
+  int pos;       // position in this workgroup's item list
+  int next;      // the item at pos + 1 (read ahead)
   int item;      // work item of matmul g
   int g;         // matmul index
   int chunk;     // chunk along K
@@ -392,7 +401,7 @@ struct Walker {
 
 template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(STREAM_WAVES, 8)))
-mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_items) {
+mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint32_t* __restrict__ sched) {
   constexpr int P = stream_steps(M, kScaleQuad);
   constexpr int T = kStreamTiles;
   constexpr int kChunkBlocks = P * kBlocksPerStep;
@@ -421,10 +430,15 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
   const int c_base = c_live ? kChunkBlocks * 64 * M + grp * 16 : kZeroOff + 16;
   const int c_stride = c_live ? MP * 4 : 0;
 
-  auto start = [&](Walker& w, int item) {
+  // This workgroup's items, ascending: items[pos] for pos in [first, end).
+  const uint32_t* items = sched + (kMaxBatchedGrid + 1);
+  const int end = (int)sched[blockIdx.x + 1];
+  auto start = [&](Walker& w, int pos, int item) {
+    w.pos = pos;
     w.item = item;
-    w.valid = item < total_items;
+    w.valid = pos < end;
     if (!w.valid) return;
+    w.next = pos + 1 < end ? (int)items[pos + 1] : 0;
     while (w.g + 1 < count && item >= table[w.g + 1].item_begin) ++w.g;
     w.chunk = 0;
     w.tile = 0;
@@ -438,7 +452,7 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
       ++n.chunk;
       n.tile = 0;
     } else {
-      start(n, w.item + (int)gridDim.x);
+      start(n, w.pos + 1, w.next);
     }
     return n;
   };
@@ -620,7 +634,10 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, int total_i
 #pragma unroll
   for (int t = 0; t < T; ++t) yacc[t] = f4{0.f, 0.f, 0.f, 0.f};
   w[0] = Walker{};
-  start(w[0], blockIdx.x);
+  {
+    const int first = (int)sched[blockIdx.x];
+    start(w[0], first, first < end ? (int)items[first] : 0);
+  }
   issue(w[0], sets[0], true);
 #pragma unroll
   for (int i = 1; i < kSets; ++i) {
@@ -718,8 +735,42 @@ BatchedLayout batched_layout(int /*M*/, int count, const int64_t* N, const int64
   BatchedLayout L{};
   for (int g = 0; g < count; ++g) L.total_items += stream_tiles(N[g]);
   L.table_bytes = align256((size_t)count * sizeof(BatchedGemv));
-  L.total_bytes = L.table_bytes;
+  L.sched_bytes = align256(((size_t)kMaxBatchedGrid + 1 + (size_t)L.total_items) * sizeof(uint32_t));
+  L.total_bytes = L.table_bytes + L.sched_bytes;
   return L;
+}
+
+void batched_schedule(int count, const int64_t* N, const int64_t* K, int grid, uint32_t* sched) {
+  struct Item { int64_t cost; uint32_t index; };
+  std::vector<Item> all;
+  for (int g = 0, item = 0; g < count; ++g) {
+    const int64_t tiles = stream_tiles(N[g]);
+    for (int64_t t = 0; t < tiles; ++t, ++item) {
+      const int64_t rows = std::min<int64_t>(64 * kStreamTiles, N[g] - t * 64 * kStreamTiles);
+      all.push_back(Item{rows * K[g], (uint32_t)item});
+    }
+  }
+  std::stable_sort(all.begin(), all.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  typedef std::pair<int64_t, int> Load;   // (assigned cost, workgroup)
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int w = 0; w < grid; ++w) heap.push(Load{0, w});
+  std::vector<std::vector<uint32_t>> lists(grid);
+  for (const Item& it : all) {
+    Load l = heap.top();
+    heap.pop();
+    lists[l.second].push_back(it.index);
+    l.first += it.cost;
+    heap.push(l);
+  }
+  uint32_t* off = sched;
+  uint32_t* items = sched + kMaxBatchedGrid + 1;
+  uint32_t pos = 0;
+  for (int w = 0; w < grid; ++w) {
+    std::sort(lists[w].begin(), lists[w].end());
+    off[w] = pos;
+    for (uint32_t i : lists[w]) items[pos++] = i;
+  }
+  for (int w = grid; w <= kMaxBatchedGrid; ++w) off[w] = pos;
 }
 
 void batched_fill_table(int /*M*/, int count, const uint16_t* const* x,
@@ -791,6 +842,7 @@ int batched_grid(int M, bool quad, int64_t total_items) {
     return 0;
   int64_t grid = (int64_t)per_cu * cus;
   if (grid > total_items) grid = total_items;
+  if (grid > kMaxBatchedGrid) grid = kMaxBatchedGrid;
   return (int)(grid < 1 ? 1 : grid);
 }
 
@@ -799,7 +851,10 @@ hipError_t launch_batched(int M, bool quad, const void* ws, int count, int total
   const void* k = batched_kernel_for(M, quad);
   if (!k) return hipErrorInvalidValue;
   const BatchedGemv* table = static_cast<const BatchedGemv*>(ws);
-  void* args[] = {(void*)&table, (void*)&count, (void*)&total_items};
+  const uint32_t* sched = reinterpret_cast<const uint32_t*>(
+      static_cast<const char*>(ws) + align256((size_t)count * sizeof(BatchedGemv)));
+  (void)total_items;
+  void* args[] = {(void*)&table, (void*)&count, (void*)&sched};
   return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, batched_lds(M, quad), s);
 }
 

@@ -219,17 +219,17 @@ int q4_gemv_batched_plan(int M, const q4w_gemv_desc* descs, int count, void* ws,
     scales[g] = descs[g].scales;
     y[g] = descs[g].y;
   }
-  std::vector<q4w::BatchedGemv> table(count);
-  q4w::batched_fill_table(M, count, x.data(), codes.data(), scales.data(), y.data(), N.data(),
-                          K.data(), ws, table.data());
-  hipError_t e = hipMemcpy(ws, table.data(), count * sizeof(q4w::BatchedGemv),
-                           hipMemcpyHostToDevice);
-  if (e == hipSuccess && L.counter_bytes > 0)
-    e = hipMemset(static_cast<char*>(ws) + L.table_bytes, 0, L.counter_bytes);
-  if (e != hipSuccess) return hip_status(e);
   const bool quad = q4w::batched_quad(count, K.data(), scales.data());
   const int grid = q4w::batched_grid(M, quad, L.total_items);
   if (grid < 1) return hip_status(hipErrorInvalidDeviceFunction);
+  // table and per-workgroup item lists, staged on the host and copied once
+  std::vector<char> host(L.total_bytes, 0);
+  q4w::batched_fill_table(M, count, x.data(), codes.data(), scales.data(), y.data(), N.data(),
+                          K.data(), ws, reinterpret_cast<q4w::BatchedGemv*>(host.data()));
+  q4w::batched_schedule(count, N.data(), K.data(), grid,
+                        reinterpret_cast<uint32_t*>(host.data() + L.table_bytes));
+  const hipError_t e = hipMemcpy(ws, host.data(), L.total_bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e);
   plan->M = M;
   plan->variant = quad ? 1 : 0;
   plan->count = count;

@@ -65,12 +65,20 @@ struct BatchedGemv {
 };
 static_assert(sizeof(BatchedGemv) == 80, "table entry layout");
 
+// Workspace layout of a batch: the table, then each persistent workgroup's
+// list of work items (uint32 offsets[kMaxBatchedGrid + 1], then the items),
+// both 256-byte aligned.
+constexpr int kMaxBatchedGrid = 4096;
 struct BatchedLayout {
-  size_t table_bytes, counter_bytes, partial_bytes, total_bytes;
+  size_t table_bytes, sched_bytes, total_bytes;
   int64_t total_items;
 };
-// Workspace layout of a batch: the table (256-byte aligned).
 BatchedLayout batched_layout(int M, int count, const int64_t* N, const int64_t* K);
+// Deals the items of a batch to `grid` workgroups, longest first, each to the
+// least loaded workgroup so far (cost: rows x K), and lists every workgroup's
+// items in ascending order.  sched: offsets[grid + 1] then items, as laid out
+// in the workspace (host memory, sched_bytes).
+void batched_schedule(int count, const int64_t* N, const int64_t* K, int grid, uint32_t* sched);
 // Fills `table` (host memory, count entries) for a workspace at device address ws.
 void batched_fill_table(int M, int count, const uint16_t* const* x, const uint8_t* const* codes,
                         const uint16_t* const* scales, uint16_t* const* y, const int64_t* N,

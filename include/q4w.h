@@ -172,10 +172,13 @@ int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
  *
  * q4w_gemv_desc: one matmul, layouts and alignments as for q4_gemv_skinny;
  *   N >= 1, K >= 32, K % 32 == 0, N <= 2^19, K <= 2^24.
- * q4_gemv_batched_ws_bytes: workspace bytes for the batch (its work
- *   table); 0 if a size or shape is invalid.
+ * q4_gemv_batched_ws_bytes: workspace bytes for the batch (its work table
+ *   and every workgroup's list of work items); 0 if a size or shape is
+ *   invalid.
  * q4_gemv_batched_plan: a set-up call, not for graph capture.  Checks every
- *   descriptor, writes the device-side work table into ws (256-byte
+ *   descriptor, deals the work items (64-row tiles x K) to the persistent
+ *   workgroups so that each gets about the same rows x K (longest first, to
+ *   the least loaded), writes the table and the lists into ws (256-byte
  *   aligned, >= q4_gemv_batched_ws_bytes bytes) and fills *plan.  It synchronizes with the device (blocking copy); the
  *   descriptor array may be freed when it returns.  The workspace then
  *   belongs to the plan until the caller stops using the plan.

@@ -55,6 +55,22 @@ def test_explicit_split_k(split):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
 
+@pytest.mark.parametrize("m", [5, 13])
+def test_explicit_split_k_matrix_core(m):
+    """Matrix-core kernel with many slices (K = 4096, split_k = 64 gives 32
+    one-step slices): the fixup's partial loads go out in several chunks
+    (18 slices per chunk at M = 5, 9 at M = 13), over a ragged last row tile."""
+    codes, scales, q, d = packed(300, 4096, 40)
+    x = synthetic.activations(m, 4096, 41 + m)
+    ref = q4.matmul(x, q, d)
+    y1 = run(x, codes, scales, 64)
+    assert_close(y1, ref, what=f"M={m} split=64")
+    y2 = run(x, codes, scales, 64)
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
+    y0 = run(x, codes, scales, 0)
+    assert_close(y0, ref, what=f"M={m} split=auto")
+
+
 def test_workspace_shared_across_shapes():
     """One workspace serving a split-K shape with few tiles, then one with many:
     the first call's partials must never be read as the second call's counters."""
