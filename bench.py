@@ -178,6 +178,25 @@ def bench_decode_step(torch, q4w, synthetic, reps, m=5):
     return out
 
 
+def bench_prefill_pass(torch, q4w, synthetic, reps, m=2048):
+    """64 layers x 5 projections on the A8 route at M = 2048 tokens: per layer
+    three activation quantizations and five GEMMs, as a HIP graph."""
+    from bit_quantized_weight_amd.prefill import PrefillPass
+    p = PrefillPass(m)
+    torch.cuda.synchronize()
+    p.run()
+    t_eager = time_region(torch, lambda: [p.run() for _ in range(reps)]) / reps
+    g = capture(torch, p.run)
+    g.replay()
+    t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
+    out = dict(M=m, layers=len(p.layers), launches_per_pass=8 * len(p.layers),
+               int_ops_per_pass=p.int_ops, ms_graph=t_graph * 1e3, ms_eager=t_eager * 1e3,
+               tok_s=m / t_graph, tops=p.int_ops / t_graph / 1e12)
+    del g, p
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_prefill(torch, q4w, synthetic, reps):
     """A8 route at M = 2048: the whole route per launch pair (activation
     quantization + GEMM), and the GEMM alone from prepared activations."""
@@ -307,6 +326,9 @@ def main():
         extra["a8w4_prefill"] = bench_prefill(torch, q4w, synthetic, reps=20)
         log(f"[bench] a8w4_prefill: route {extra['a8w4_prefill']['ms_route']:.3f} ms "
             f"({extra['a8w4_prefill']['tok_s']:.0f} tok/s), GEMM {extra['a8w4_prefill']['ms_gemm']:.3f} ms")
+        extra["a8w4_prefill_pass_64L"] = bench_prefill_pass(torch, q4w, synthetic, reps=3)
+        log(f"[bench] a8w4_prefill_pass_64L: {extra['a8w4_prefill_pass_64L']['ms_graph']:.2f} ms "
+            f"({extra['a8w4_prefill_pass_64L']['tok_s']:.0f} tok/s)")
 
     steps = args.steps
     t = dec["t_graph_s"]
