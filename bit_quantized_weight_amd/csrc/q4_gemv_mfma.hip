@@ -58,6 +58,7 @@ constexpr int kThreads = 64 * kWaves;
 // Split-K fixup: partial loads in flight per thread.  A 64-row tile at M <= 8
 // has at most 2 outputs per thread, so S <= 18 slices take one round.
 constexpr int kFixupBatch = 36;
+constexpr int kMinMfmaWgs = 256;             // one workgroup per CU
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kBlocksPerStep = 4;            // one 128-bit load per lane = 4 blocks per lane group set
@@ -694,8 +695,10 @@ hipError_t launch_mfma_m(const uint16_t* x, const uint8_t* codes, const uint16_t
 }  // namespace
 
 // Split plan of the matrix-core kernel: slices are whole 4-block steps, at
-// most one ring (kMaxSliceSteps) long, with enough slices to put about four
-// workgroups on every CU.
+// most one ring (kMaxSliceSteps) long, so S is at least steps / 8.  More
+// slices are added only below kMinMfmaWgs workgroups: the split-K fixup chain
+// costs more than the extra parallelism buys (out 5120 -> 5120 at M = 5:
+// 10 slices 9.8 us, 5 slices 8.9 us).
 SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
   SkinnyPlan p{};
   p.route = kRouteMfma;
@@ -712,8 +715,7 @@ SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k) {
   } else {
     int max_steps = lds_steps;
     int S = (steps_total + max_steps - 1) / max_steps;
-    const int target_wgs = 1024;
-    while ((int64_t)S * p.row_tiles < target_wgs && steps_total / (S + 1) >= 2) ++S;
+    while ((int64_t)S * p.row_tiles < kMinMfmaWgs && steps_total / (S + 1) >= 1) ++S;
     steps = (steps_total + S - 1) / S;
   }
   if (steps < 1) steps = 1;

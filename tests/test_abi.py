@@ -133,6 +133,11 @@ def test_gemv_split_policy(L):
     # every width up to 16 (two activation staging items per thread past M = 8)
     for m in (4, 5, 8, 9, 13, 16):
         assert slices(m, 5120, 17408) == 17, m
+    # ... and no more than that at or above 256 workgroups (64 rows each)
+    assert slices(5, 5120, 5120) == 5          # 80 row tiles x 5 = 400 workgroups
+    assert slices(5, 7168, 5120) == 5
+    assert slices(5, 17408, 5120) == 5
+    assert slices(5, 512, 5120) == 20          # 8 row tiles: 32 wanted, 2-step slices give 20
 
 
 def test_act_quant_checks(L):

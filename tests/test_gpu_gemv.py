@@ -1,4 +1,4 @@
-"""q4_gemv_skinny on the GPU against the fp64 oracle (M = 1..8)."""
+"""q4_gemv_skinny on the GPU against the fp64 oracle (M = 1..16)."""
 
 import functools
 
