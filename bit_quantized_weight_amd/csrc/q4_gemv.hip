@@ -87,15 +87,22 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 // (This kernel serves M = 1..3; wider M goes to the matrix-core kernel.)
 __host__ __device__ constexpr int rows_per_lane(int) { return 2; }
 // Steps requested at once per wave (the register ring).
-__host__ __device__ constexpr int ring_steps(int M) { return M == 1 ? 6 : 4; }
+__host__ __device__ constexpr int ring_steps(int M) { return M <= 2 ? 6 : 5; }
+// Longest slice when a row must be split: above M = 1 more workgroups pay off
+// (verify_down M = 2: 5 slices of 4 steps 14.2 us, 3 slices of 6 steps 15.2 us).
+__host__ __device__ constexpr int split_steps(int M) { return M == 1 ? 6 : 4; }
+constexpr int kShortSlice = 4;           // depth of the short no-refill form
 // Occupancy target (waves per SIMD).
 __host__ __device__ constexpr int waves_per_simd(int) { return 4; }
 // Largest slice (blocks): whole steps, within the LDS budget and at most two
-// rings long; and the (row, block) staging items per thread it needs.
+// rings long (one at M = 3); and the (row, block) staging items per thread it
+// needs.
+__host__ __device__ constexpr int max_ring_rounds(int M) { return M == 3 ? 1 : 2; }   // M = 3's ring form would spill
 __host__ __device__ constexpr int max_slice_blocks(int M) {
-  return (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow < 2 * ring_steps(M) * kLanesPerRow
+  return (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow <
+                 max_ring_rounds(M) * ring_steps(M) * kLanesPerRow
              ? (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow
-             : 2 * ring_steps(M) * kLanesPerRow;
+             : max_ring_rounds(M) * ring_steps(M) * kLanesPerRow;
 }
 __host__ __device__ constexpr int stage_items(int M) {
   return (M * max_slice_blocks(M) + kThreads - 1) / kThreads;
@@ -104,7 +111,10 @@ __host__ __device__ constexpr int stage_items(int M) {
 namespace {
 
 // kRing = false: every slice fits the ring (steps <= P), one pass, no refills.
-template <int M, bool kRing>
+// P: steps of loads in flight per wave (the register ring).  The no-refill
+// form is built at two depths: a slice of at most kShortSlice steps takes the
+// short one (fewer registers, more waves per SIMD).
+template <int M, bool kRing, int P>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(M), 8)))
 skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
@@ -112,7 +122,6 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
               float* __restrict__ partial, uint32_t* __restrict__ counters,
               int N, int K, int bps, int S) {
   constexpr int RL = rows_per_lane(M);
-  constexpr int P = ring_steps(M);
   constexpr int kRowsPerWg = kWaves * kSlots * RL;
   extern __shared__ uint4 smem[];
 
@@ -167,7 +176,12 @@ skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
   // They are needed before any weight step, and loads complete in issue
   // order, so they go out ahead of the weight loads.  Blocks past the slice
   // read zeros (out-of-range offset, no memory request).
-  constexpr int kItems = stage_items(M);
+  // (row, block) staging items per thread: a no-refill slice is at most P
+  // steps.  At least two: with one, the compiler issues these loads after
+  // the weight loads (measured: +0.4 to +0.9 us at M = 1).
+  constexpr int kItems = kRing ? stage_items(M)
+                               : ((M * P * kLanesPerRow + kThreads - 1) / kThreads > 2
+                                      ? (M * P * kLanesPerRow + kThreads - 1) / kThreads : 2);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, 0, M * K * 2, kRsrcWord3);
   uint4 raw[kItems][4];
@@ -350,14 +364,25 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
     counters = reinterpret_cast<uint32_t*>(ws);
     partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.counter_bytes);
   }
-  const bool ring = bpad / kLanesPerRow > ring_steps(M);
-  if (ring)
-    hipLaunchKernelGGL((skinny_kernel<M, true>), dim3(p.row_tiles, p.splits), dim3(kThreads), lds,
-                       s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
+  const int steps = bpad / kLanesPerRow;
+  const bool ring = steps > ring_steps(M);   // never when a slice is one ring at most
+  if constexpr (max_ring_rounds(M) > 1) {
+    if (ring) {
+      hipLaunchKernelGGL((skinny_kernel<M, true, ring_steps(M)>), dim3(p.row_tiles, p.splits), dim3(kThreads), lds,
+                         s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
+                         (int)N, (int)K, p.blocks_per_split, p.splits);
+      return hipGetLastError();
+    }
+  } else if (ring) {
+    return hipErrorInvalidValue;
+  }
+  if (steps <= kShortSlice)
+    hipLaunchKernelGGL((skinny_kernel<M, false, kShortSlice>), dim3(p.row_tiles, p.splits), dim3(kThreads),
+                       lds, s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
                        (int)N, (int)K, p.blocks_per_split, p.splits);
   else
-    hipLaunchKernelGGL((skinny_kernel<M, false>), dim3(p.row_tiles, p.splits), dim3(kThreads), lds,
-                       s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
+    hipLaunchKernelGGL((skinny_kernel<M, false, ring_steps(M)>), dim3(p.row_tiles, p.splits), dim3(kThreads),
+                       lds, s, x, reinterpret_cast<const uint4*>(codes), scales, y, partial, counters,
                        (int)N, (int)K, p.blocks_per_split, p.splits);
   return hipGetLastError();
 }
@@ -385,12 +410,13 @@ SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
     // stores, the arrival count, the last workgroup's partial loads).  On the
     // measured shapes that chain costs more than one ring refill, and more
     // than running with as few as one workgroup per CU, so: one slice when
-    // the row fits two rings, else the fewest slices that need no refill;
-    // more slices only below kMinSkinnyWgs workgroups.
+    // the row fits the largest slice, else slices of split_steps(M) steps
+    // (within one ring: no refill); more slices only below kMinSkinnyWgs
+    // workgroups.
     const int steps_total = (nb + kLanesPerRow - 1) / kLanesPerRow;
-    const int max_steps = lds_blocks / kLanesPerRow;            // two rings, or the LDS budget
-    const int ring = ring_steps(M);
-    int S = steps_total <= max_steps ? 1 : (steps_total + ring - 1) / ring;
+    const int max_steps = lds_blocks / kLanesPerRow;            // largest slice
+    const int sl = split_steps(M);
+    int S = steps_total <= max_steps ? 1 : (steps_total + sl - 1) / sl;
     while ((int64_t)S * p.row_tiles < kMinSkinnyWgs && steps_total / (S + 1) >= 1) ++S;
     bps = ((steps_total + S - 1) / S) * kLanesPerRow;
   }

@@ -118,12 +118,18 @@ def test_gemv_split_policy(L):
         assert (b - region) % (m * n * 4) == 0, (m, n, k, b)
         return (b - region) // (m * n * 4)
 
-    # VALU kernel (M <= 3): one slice when a row fits two register rings ...
+    # VALU kernel (M <= 3): one slice when a row fits the largest slice
+    # (12 steps at M = 1, 11 at M = 2 (LDS), 5 at M = 3) ...
     assert slices(1, 17408, 5120) == 1        # decode gate/up
     assert slices(1, 7168, 5120) == 1         # qkv
     assert slices(1, 5120, 5120) == 1         # out
     assert slices(2, 17408, 5120) == 1
-    # ... else the fewest slices that need no ring refill (6 steps at M = 1, 4 above)
+    assert slices(1, 4100, 12256) == 1        # 12 steps
+    assert slices(2, 4100, 11232) == 1        # 11 steps
+    assert slices(2, 4100, 12256) == 3        # 12 steps: slices of 4
+    assert slices(3, 4100, 5088) == 1         # 5 steps
+    assert slices(3, 4100, 6112) == 2         # 6 steps: slices of 4
+    # ... else slices of 6 steps at M = 1, 4 above (within the ring: no refill)
     assert slices(1, 5120, 17408) == 3        # verify down: 17 steps of 32 blocks
     assert slices(2, 5120, 17408) == 5
     assert slices(3, 5120, 17408) == 5

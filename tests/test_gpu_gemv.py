@@ -222,6 +222,35 @@ def test_large_n_split_counters(m):
     assert_close(y[:, rows], q4.matmul(x, q, d), what=f"N={n} M={m} split 2")
 
 
+@functools.lru_cache(maxsize=2)
+def packed_sampled(n, k, seed, rows):
+    """Weights generated and packed on the GPU; the oracle quantizes only the
+    sampled rows (quantization is per row, so they match the full pack)."""
+    torch = torch_cuda()
+    w = synthetic.weights_device(n, k, seed)
+    wr = w.index_select(0, torch.as_tensor(rows, device="cuda")).cpu().numpy()
+    codes, scales = pack(w)
+    del w
+    q, d = q4.quantize(wr)
+    return codes, scales, q, d
+
+
+@pytest.mark.parametrize("k", [992, 4064, 5088, 6112, 7136, 9184, 11232, 12256])
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_vector_kernel_slice_forms(m, k):
+    """Every form of the M <= 3 kernel on one slice per row tile (N = 4100:
+    257 tiles of 16 rows): 1 to 12 steps of 32 blocks, each step count with a
+    ragged last step, covering the short no-refill form, the full-depth one,
+    the refilled ring and, at M = 3 past 5 steps, the split into slices."""
+    n = 4100
+    rows = tuple(np.unique(np.concatenate([[0, 15, 16, n - 1],
+                                           np.random.default_rng(k).integers(0, n, 60)])).tolist())
+    codes, scales, q, d = packed_sampled(n, k, 90, rows)
+    x = synthetic.activations(m, k, 91 + m)
+    y = run(x, codes, scales)
+    assert_close(y[:, list(rows)], q4.matmul(x, q, d), what=f"M={m} K={k} N={n}")
+
+
 BATCH_SHAPES = [(100, 96), (300, 1056), (257, 5120), (70, 8192), (5120, 17408), (64, 512)]
 
 
