@@ -66,7 +66,11 @@ constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks
 // LDS per block of the slice: the M activation rows as A-operand octets
 // (4 slot groups x M rows x 16 bytes) and the -bias of rows 0..Mp4-1
 // (Mp4 = M rounded up to 4; rows >= M hold 0).  A-operand rows M..15 are
-// not stored: their lanes read a shared zero octet instead.
+// not stored: their lanes read row 0's octets instead.  Row m of an MFMA
+// product depends on A row m only, and rows >= M are never stored, so what
+// those lanes read does not matter; reading in-bounds data at the same
+// stride as every other lane keeps each LDS address a per-lane base plus a
+// constant offset.
 __host__ __device__ constexpr int mp4(int M) { return (M + 3) / 4 * 4; }
 __host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * mp4(M); }
 // Steps of a K-chunk whose (block, row) staging items fit kItems per thread,
@@ -81,10 +85,7 @@ __host__ __device__ constexpr int max_slice_steps(int M) { return chunk_steps(M,
 __host__ __device__ constexpr int stage_items(int M) {
   return (max_slice_steps(M) * kBlocksPerStep * mp4(M) + kThreads - 1) / kThreads;
 }
-constexpr int kLdsZeroBytes = 32;            // one zero octet + one zero float4
-__host__ __device__ constexpr int lds_bytes(int M, int bpad) {
-  return bpad * lds_bytes_per_block(M) + kLdsZeroBytes;
-}
+__host__ __device__ constexpr int lds_bytes(int M, int bpad) { return bpad * lds_bytes_per_block(M); }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -230,7 +231,6 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   char* lds = reinterpret_cast<char*>(smem);
   uint4* xs = smem;                                                    // [bpad][4][M]
   float* cl = reinterpret_cast<float*>(lds + bpad * 64 * M);           // [bpad][MP]
-  const int zero_off = bpad * lds_bytes_per_block(M);                  // zero octet, zero float4
   const uint32_t k1032 = 0x64086408u;
   const uint32_t k72 = 0x54805480u;
 #pragma unroll
@@ -257,18 +257,16 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
       cl[sb * MP + sm] = -c;               // rows >= M read zeros, so c == 0 there
     }
   }
-  if (tid < 2) reinterpret_cast<uint4*>(lds + zero_off)[tid] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   // Per-lane LDS addresses: A octet of block b at a_base + b * a_stride
-  // (rows >= M: the zero octet, stride 0), bias float4 of rows 4 grp.. at
-  // c_base + b * c_stride (groups past Mp4: the zero float4).
-  const bool a_live = col < M;
-  const int a_base = a_live ? (grp * M + col) * 16 : zero_off;
-  const int a_stride = a_live ? 64 * M : 0;
-  const bool c_live = 4 * grp < MP;
-  const int c_base = c_live ? bpad * 64 * M + grp * 16 : zero_off + 16;
-  const int c_stride = c_live ? MP * 4 : 0;
+  // (rows >= M read row 0), bias float4 of rows 4 grp.. at c_base +
+  // b * c_stride (groups past Mp4 read group 0's).  The strides are
+  // constants, so the compiler folds b * stride into the LDS instruction.
+  const int a_base = (grp * M + (col < M ? col : 0)) * 16;
+  constexpr int a_stride = 64 * M;
+  const int c_base = bpad * 64 * M + (4 * grp < MP ? grp : 0) * 16;
+  constexpr int c_stride = MP * 4;
 
   f4 yacc[R];
 #pragma unroll
@@ -409,7 +407,6 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
   constexpr int MP = mp4(M);
   constexpr int RM = M < 4 ? M : 4;
   constexpr int kLdsBuf = lds_bytes(M, kChunkBlocks);
-  constexpr int kZeroOff = kChunkBlocks * lds_bytes_per_block(M);
   constexpr int kSets = 2;
   static_assert(T % kSets == 0, "units cycle through register sets and tiles together");
   extern __shared__ uint4 smem[];
@@ -424,12 +421,10 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
   const int rl = wave * 16 + col;          // tile-local weight row of this lane
 
   // Per-lane LDS addresses (see mfma_item), for a buffer of kChunkBlocks blocks.
-  const bool a_live = col < M;
-  const int a_base = a_live ? (grp * M + col) * 16 : kZeroOff;
-  const int a_stride = a_live ? 64 * M : 0;
-  const bool c_live = 4 * grp < MP;
-  const int c_base = c_live ? kChunkBlocks * 64 * M + grp * 16 : kZeroOff + 16;
-  const int c_stride = c_live ? MP * 4 : 0;
+  const int a_base = (grp * M + (col < M ? col : 0)) * 16;
+  constexpr int a_stride = 64 * M;
+  const int c_base = kChunkBlocks * 64 * M + (4 * grp < MP ? grp : 0) * 16;
+  constexpr int c_stride = MP * 4;
 
   // This workgroup's items, ascending: items[pos] for pos in [first, end).
   const uint32_t* items = sched + (kMaxBatchedGrid + 1);
@@ -623,10 +618,6 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
     }
   };
 
-  // zero octet and zero float4 of both LDS buffers
-  if (tid < 4)
-    reinterpret_cast<uint4*>(reinterpret_cast<char*>(smem) + (tid >> 1) * kLdsBuf + kZeroOff)[tid & 1] =
-        make_uint4(0, 0, 0, 0);
   char* lds0 = reinterpret_cast<char*>(smem);
 
   Set sets[kSets];
