@@ -178,23 +178,30 @@ def bench_decode_step(torch, q4w, synthetic, reps, m=5):
     return out
 
 
-def bench_prefill_pass(torch, q4w, synthetic, reps, m=2048):
-    """64 layers x 5 projections on the A8 route at M = 2048 tokens: per layer
-    three activation quantizations and five GEMMs, as a HIP graph."""
+def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
+    """64 layers x 5 projections on the A8 route at M = 512, 1024 and 2048
+    tokens (one packed weight set): per layer three activation quantizations
+    and five GEMMs, as a HIP graph."""
     from bit_quantized_weight_amd.prefill import PrefillPass
-    p = PrefillPass(m)
-    torch.cuda.synchronize()
-    p.run()
-    t_eager = time_region(torch, lambda: [p.run() for _ in range(reps)]) / reps
-    g = capture(torch, p.run)
-    g.replay()
-    t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
-    out = dict(M=m, layers=len(p.layers), launches_per_pass=8 * len(p.layers),
-               int_ops_per_pass=p.int_ops, ms_graph=t_graph * 1e3, ms_eager=t_eager * 1e3,
-               tok_s=m / t_graph, tops=p.int_ops / t_graph / 1e12)
-    del g, p
+    weights = None
+    per_m = {}
+    for m in ms:
+        p = PrefillPass(m, weights=weights)
+        weights = p.layers
+        torch.cuda.synchronize()
+        p.run()
+        t_eager = time_region(torch, lambda: [p.run() for _ in range(reps)]) / reps
+        g = capture(torch, p.run)
+        g.replay()
+        t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
+        per_m[str(m)] = dict(int_ops_per_pass=p.int_ops, ms_graph=t_graph * 1e3, ms_eager=t_eager * 1e3,
+                             tok_s=m / t_graph, tops=p.int_ops / t_graph / 1e12)
+        layers = len(p.layers)
+        del g, p
+        torch.cuda.empty_cache()
+    del weights
     torch.cuda.empty_cache()
-    return out
+    return dict(layers=layers, launches_per_pass=8 * layers, per_M=per_m)
 
 
 def bench_prefill(torch, q4w, synthetic, reps):
@@ -327,8 +334,8 @@ def main():
         log(f"[bench] a8w4_prefill: route {extra['a8w4_prefill']['ms_route']:.3f} ms "
             f"({extra['a8w4_prefill']['tok_s']:.0f} tok/s), GEMM {extra['a8w4_prefill']['ms_gemm']:.3f} ms")
         extra["a8w4_prefill_pass_64L"] = bench_prefill_pass(torch, q4w, synthetic, reps=3)
-        log(f"[bench] a8w4_prefill_pass_64L: {extra['a8w4_prefill_pass_64L']['ms_graph']:.2f} ms "
-            f"({extra['a8w4_prefill_pass_64L']['tok_s']:.0f} tok/s)")
+        for m_, r_ in extra["a8w4_prefill_pass_64L"]["per_M"].items():
+            log(f"[bench] a8w4_prefill_pass_64L M={m_}: {r_['ms_graph']:.2f} ms ({r_['tok_s']:.0f} tok/s)")
 
     steps = args.steps
     t = dec["t_graph_s"]

@@ -170,6 +170,7 @@ constexpr int kMSub = kTM / 32;   // 32-row MFMA subtiles per workgroup
 constexpr int kNSub = kTN / 32;   // 32-column MFMA subtiles per workgroup
 constexpr float kMagic = 12582912.0f;   // 0x4B400000 = 1.5 * 2^23
 constexpr int kSdStride = kTN + 16;       // padding spreads the staging writes over all banks
+constexpr int kA8NarrowTiles = 256;      // fewer 128-row tiles than CUs: use 64-row tiles
 
 __device__ __forceinline__ uint32_t lo_codes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_codes(uint32_t w) { return w & 0xF0F0F0F0u; }
@@ -192,7 +193,9 @@ struct ChunkLds {
   float sa[kChunkGroups * kTM];
 };
 
-template <bool kDebug>
+// kMS: 32-row M subtiles per workgroup, 4 (128 x 128 tiles) or 2 (64 x 128
+// tiles, twice the workgroups for short prompts); each wave takes kMS / 2.
+template <bool kDebug, int kMS>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
@@ -201,6 +204,9 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
                  int mtiles, int ntiles) {
   __shared__ ChunkLds lds[2];
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  static_assert(kMS == 2 || kMS == 4, "64- or 128-row tiles");
+  constexpr int TM = 32 * kMS;      // rows (tokens) of this workgroup's tile
+  constexpr int kMI = kMS / 2;      // 32-row subtiles per wave
 
   const int nb = K / kBlock;
   const int G = K / kActGroup;
@@ -223,22 +229,22 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   const int j = lane & 31;
   const int h = lane >> 5;
   const int n_base = nt * kTN;
-  const int mt32 = mt * kMSub;       // first 32-row activation tile of the workgroup
+  const int mt32 = mt * kMS;         // first 32-row activation tile of the workgroup
 
   // ---- buffer resources (out-of-range offsets read zeros, no traffic) ----
   const int rows_here = min(kTN, N - n_base);
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(codes + (size_t)n_base * nb), 0, rows_here * nb * kBlockBytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(xq_t + (size_t)mt32 * nb * 64), 0, kMSub * nb * 64 * 16, 0x00020000);
+      (void*)(xq_t + (size_t)mt32 * nb * 64), 0, kMS * nb * 64 * 16, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(sa_t + (size_t)mt32 * G * 32), 0, kMSub * G * 32 * 4, 0x00020000);
+      (void*)(sa_t + (size_t)mt32 * G * 32), 0, kMS * G * 32 * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scales + (size_t)n_base * nb), 0, rows_here * nb * 2, 0x00020000);
 
   // ---- cooperative chunk staging --------------------------------------------
-  // per thread: 2 weight units (row, block), 4 activation units, 2 scales, 1 sa
-  uint4 rawb[2], rawa[4];
+  // per thread: 2 weight units (row, block), kMS activation units, 2 scales, 1 sa
+  uint4 rawb[2], rawa[kMS];
   uint32_t rawd[2];
   float rawsa;
   auto stage_issue = [&](int c) {
@@ -252,8 +258,8 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
       rawb[it] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int u = it * 256 + tid;          // 4 m-subtiles x 4 blocks x 64 lanes
+    for (int it = 0; it < kMS; ++it) {
+      const int u = it * 256 + tid;          // kMS m-subtiles x 4 blocks x 64 lanes
       const int ms = u >> 8, bl = (u >> 6) & 3, l = u & 63;
       const int b = c * kChunkBlocks + bl;
       const uint32_t off = (b < nb) ? (uint32_t)(((ms * nb + b) * 64 + l) * 16) : 0x80000000u;
@@ -270,10 +276,11 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
         rawd[it] = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
       }
       {
-        const int gi = tid >> 7, r = tid & 127;  // 2 groups x 128 rows
+        const int gi = tid / TM, r = tid % TM;  // 2 groups x TM rows
         const int g = c * kChunkGroups + gi;
         const int ms = r >> 5, rr = r & 31;
-        const uint32_t off = (g < G) ? (uint32_t)(((ms * G + g) * 32 + rr) * 4) : 0x80000000u;
+        const uint32_t off = (gi < kChunkGroups && g < G) ? (uint32_t)(((ms * G + g) * 32 + rr) * 4)
+                                                          : 0x80000000u;
         rawsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
       }
     }
@@ -292,7 +299,7 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
           make_uint4(lo_codes(w.z), hi_codes(w.z), lo_codes(w.w), hi_codes(w.w));
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) L.aq[it * 256 + tid] = rawa[it];
+    for (int it = 0; it < kMS; ++it) L.aq[it * 256 + tid] = rawa[it];
     if (!kDebug) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
@@ -305,7 +312,7 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
         const float dn = __shfl_xor(d, 1, 64);
         if ((bl & 1) == 0) L.sb[(bl >> 1) * kTN + r] = -kMagic * (d + dn);
       }
-      L.sa[tid] = rawsa;
+      if (tid < kChunkGroups * TM) L.sa[tid] = rawsa;
     }
   };
 
@@ -313,9 +320,9 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 #pragma unroll
   for (int v = 0; v < 16; ++v) magic[v] = 0x4B400000;
 
-  float acc[2][2][16];
+  float acc[kMI][2][16];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kMI; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -327,14 +334,14 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 
   // Per-lane LDS byte offsets inside a chunk buffer; every operand read of
   // the unrolled group loop below is one of these plus a compile-time offset.
-  const int off_a = (int)offsetof(ChunkLds, aq) + ((wm * 2 * kChunkBlocks) * 64 + lane) * 16;
+  const int off_a = (int)offsetof(ChunkLds, aq) + ((wm * kMI * kChunkBlocks) * 64 + lane) * 16;
   int off_b[kChunkBlocks];
 #pragma unroll
   for (int bl = 0; bl < kChunkBlocks; ++bl)
     off_b[bl] = (int)offsetof(ChunkLds, bq) + ((wn * 2 * kChunkBlocks) * 64 + (lane ^ (4 * bl))) * 16;
   const int off_sd = (int)offsetof(ChunkLds, sd) + (wn * 64 + j) * 4;
   const int off_sb = (int)offsetof(ChunkLds, sb) + (wn * 64 + j) * 4;
-  const int off_sa = (int)offsetof(ChunkLds, sa) + (wm * 64 + 4 * h) * 4;
+  const int off_sa = (int)offsetof(ChunkLds, sa) + (wm * 32 * kMI + 4 * h) * 4;
 
 #pragma unroll 1
   for (int c = 0; c < nchunks; ++c) {
@@ -345,10 +352,10 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
       const int g = c * kChunkGroups + gi;
       if (g < G) {   // also keeps the scheduler from interleaving groups (registers)
         const int bl0 = 2 * gi;
-        v4i av[2][2];
-        float sav[2][16];
+        v4i av[kMI][2];
+        float sav[kMI][16];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
+        for (int mi = 0; mi < kMI; ++mi) {
 #pragma unroll
           for (int bi = 0; bi < 2; ++bi) {
             const uint4 t = *reinterpret_cast<const uint4*>(
@@ -359,7 +366,7 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float4 f = *reinterpret_cast<const float4*>(
-                  L + off_sa + (gi * kTM + mi * 32 + 8 * r) * 4);
+                  L + off_sa + (gi * TM + mi * 32 + 8 * r) * 4);
               sav[mi][4 * r + 0] = f.x; sav[mi][4 * r + 1] = f.y;
               sav[mi][4 * r + 2] = f.z; sav[mi][4 * r + 3] = f.w;
             }
@@ -381,14 +388,14 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
             nc = *reinterpret_cast<const float*>(L + off_sb + (gi * kTN + ni * 32) * 4);
           }
 #pragma unroll
-          for (int mi = 0; mi < 2; ++mi) {
+          for (int mi = 0; mi < kMI; ++mi) {
             const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][0], bv0, magic, 0, 0, 0);
             const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][1], bv1, magic, 0, 0, 0);
             if (kDebug) {
               const int ncol = n_base + col;
 #pragma unroll
               for (int v = 0; v < 16; ++v) {
-                const int mrow = (mt32 + wm * 2 + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int mrow = (mt32 + wm * kMI + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (mrow < M && ncol < N) {
                   int32_t* o = acc_dbg + ((size_t)mrow * N + ncol) * nb + 2 * g;
                   o[0] = (D0[v] - 0x4B400000) >> 4;
@@ -412,13 +419,13 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 
   if (kDebug) return;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
       const int ncol = n_base + (wn * 2 + ni) * 32 + j;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int mrow = (mt32 + wm * 2 + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int mrow = (mt32 + wm * kMI + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
         if (mrow < M && ncol < N)
           y[(size_t)mrow * N + ncol] = __half_as_ushort(__float2half_rn(acc[mi][ni][v]));
       }
@@ -460,17 +467,25 @@ hipError_t launch_a8w4_gemm(const void* ws, const uint8_t* codes, const uint16_t
   const int64_t mp = a8_padded_rows(M);
   const uint4* xq_t = reinterpret_cast<const uint4*>(ws);
   const float* sa_t = reinterpret_cast<const float*>(static_cast<const char*>(ws) + align256((size_t)mp * K));
-  const int mtiles = (int)(mp / kTM);
   const int ntiles = (int)((N + kTN - 1) / kTN);
+  // 64-row tiles when 128-row tiles would leave CUs idle (measured at M = 512:
+  // qkv 81 -> 71 us, out 75 -> 63, down 239 -> 205; at 320..448 tiles the
+  // 128-row form stays faster)
+  const bool narrow = (mp / kTM) * ntiles < kA8NarrowTiles;
+  const int mtiles = (int)(mp / (narrow ? kTM / 2 : kTM));
   const dim3 grid((unsigned)(mtiles * ntiles));
-  if (acc_debug)
-    hipLaunchKernelGGL(a8w4_gemm_kernel<true>, grid, dim3(256), 0, s, xq_t, sa_t,
-                       reinterpret_cast<const uint4*>(codes), scales, y, acc_debug, (int)M, (int)N,
-                       (int)K, mtiles, ntiles);
-  else
-    hipLaunchKernelGGL(a8w4_gemm_kernel<false>, grid, dim3(256), 0, s, xq_t, sa_t,
-                       reinterpret_cast<const uint4*>(codes), scales, y, acc_debug, (int)M, (int)N,
-                       (int)K, mtiles, ntiles);
+#define Q4W_A8_LAUNCH(DBG, MS)                                                                    \
+  hipLaunchKernelGGL((a8w4_gemm_kernel<DBG, MS>), grid, dim3(256), 0, s, xq_t, sa_t,             \
+                     reinterpret_cast<const uint4*>(codes), scales, y, acc_debug, (int)M, (int)N, \
+                     (int)K, mtiles, ntiles)
+  if (acc_debug) {
+    if (narrow) Q4W_A8_LAUNCH(true, 2);
+    else Q4W_A8_LAUNCH(true, 4);
+  } else {
+    if (narrow) Q4W_A8_LAUNCH(false, 2);
+    else Q4W_A8_LAUNCH(false, 4);
+  }
+#undef Q4W_A8_LAUNCH
   return hipGetLastError();
 }
 

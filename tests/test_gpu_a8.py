@@ -80,6 +80,25 @@ def test_a8_gemm_vs_oracle(m, n, k):
     assert_close(host(y), a8.prefill(x, q, d), what=f"A8 M={m} N={n} K={k}")
 
 
+@pytest.mark.parametrize("n", [16000, 16500])
+def test_tile_forms_block_sums_and_gemm(n):
+    """Both workgroup tile forms at M = 130 (two 128-row tiles): N = 16000 gives
+    250 tiles of 128 x 128, below one per CU, so the 64-row form runs (with a
+    half-empty and an empty 64-row tile); N = 16500 gives 258 and the 128-row
+    form runs, with a ragged last column tile.  Block sums bit-exact, result
+    against the A8 oracle."""
+    torch = torch_cuda()
+    m, k = 130, 192
+    codes, scales, q, d = _packed(n, k, 800 + n)
+    x = synthetic.activations(m, k, 801)
+    acc = a8w4_debug_block_acc(dev(x, torch), codes, scales)
+    y = a8w4_gemm(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    qa, _ = a8.quantize_act(x)
+    assert np.array_equal(host(acc), a8.block_sums(qa, q).astype(np.int32))
+    assert_close(host(y), a8.prefill(x, q, d), what=f"A8 M={m} N={n} K={k}")
+
+
 def test_prepare_then_gemm_matches_one_call():
     """Quantize once, reuse for two weight matrices; bit-identical to the one-call route."""
     torch = torch_cuda()
