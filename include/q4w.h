@@ -115,7 +115,15 @@ int a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
  *   with the rescale in fp32.
  *   x [M, K] fp16 16-byte aligned; y [M, N] fp16 4-byte aligned.
  *   K % 64 == 0 and K <= 2^24 (else UNSUPPORTED_SHAPE); any M, N >= 1.
- *   ws: at least a8w4_ws_bytes(M, K) bytes, 256-byte aligned.
+ *   ws: at least a8w4_ws_bytes(M, K) bytes, 256-byte aligned.  It holds the
+ *   quantized activations and, once M rounded up to 128 reaches 256 rows, a
+ *   64 MiB region (arrival counters, then fp32 partial tiles) that the GEMM
+ *   uses when its 128 x 128 tiles make a little more than one round of the
+ *   GPU's resident workgroups: the K range of every tile is then shared
+ *   evenly by all workgroups and the shared tiles are summed in a fixed
+ *   order (results are deterministic).  The quantization step zeroes the
+ *   counters and every GEMM leaves them zeroed; calls that share a
+ *   workspace must not overlap in time.
  *   M == 0 or N == 0: OK, nothing enqueued.  K == 0: y filled with zeros.
  */
 size_t a8w4_ws_bytes(int64_t M, int64_t K);
