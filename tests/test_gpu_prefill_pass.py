@@ -1,6 +1,7 @@
 """Full 64-layer prefill weight pass on the A8 route at M = 2048 tokens:
 sampled tokens x sampled output rows of the first and last layers against the
-A8 oracle, and a repeated pass bit-identical to the first."""
+A8 oracle (gate and up run as one GEMM), and a repeated pass bit-identical to
+the first."""
 
 import numpy as np
 import pytest
@@ -43,7 +44,7 @@ def _check_layer(p, layer):
         rows = _rows(n, 100 * layer + pi)
         q, d = q4.quantize(p.kept[(layer, pi)])
         ref = a8.prefill(xs[INPUT_OF[name]][TOKENS], q, d)      # [tokens, rows]
-        got = host(p.ys[pi])[TOKENS][:, rows]
+        got = host(p.output(layer, pi))[TOKENS][:, rows]
         assert_close(got, ref, what=f"prefill layer {layer} {name}")
 
 
@@ -61,10 +62,22 @@ def test_prefill_whole_pass_and_repeat(prefill_pass):
     prefill_pass.run()
     torch.cuda.synchronize()
     _check_layer(prefill_pass, CHECK_LAYERS[-1])
-    first = [host(y).copy() for y in prefill_pass.ys]
-    for y in prefill_pass.ys:
+    last = CHECK_LAYERS[-1]
+    outs = [prefill_pass.output(last, pi) for pi in range(len(synthetic.LAYER_PROJECTIONS))]
+    first = [host(y).copy() for y in outs]
+    for y in outs:
         y.fill_(7.0)
     prefill_pass.run()
     torch.cuda.synchronize()
-    for pi, (a, y) in enumerate(zip(first, prefill_pass.ys)):
+    for pi, (a, y) in enumerate(zip(first, outs)):
         assert np.array_equal(a.view(np.uint16), host(y).view(np.uint16)), pi
+
+
+def test_gate_up_run_as_one_gemm(prefill_pass):
+    """The pass packs each layer's gate and up weights back to back and runs
+    them as one GEMM: the per-projection outputs are views of one buffer."""
+    assert all(f is not None for f in prefill_pass.fused)
+    g = prefill_pass.output(0, 2)
+    u = prefill_pass.output(0, 3)
+    assert g.data_ptr() == prefill_pass.y_gate_up.data_ptr()
+    assert u.data_ptr() == prefill_pass.y_gate_up.data_ptr() + g.shape[1] * 2
