@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 // Rows per lane: more rows re-use the activation registers more (less LDS
 // traffic per weight) at the cost of registers and of fewer workgroups.
-// (This kernel serves M = 1..3; wider M goes to the matrix-core kernel.)
+// (This kernel serves M = 1..4; wider M goes to the matrix-core kernel.)
 __host__ __device__ constexpr int rows_per_lane(int) { return 2; }
 // Steps requested at once per wave (the register ring).
 __host__ __device__ constexpr int ring_steps(int M) { return M <= 2 ? 6 : 5; }
@@ -92,12 +92,12 @@ __host__ __device__ constexpr int ring_steps(int M) { return M <= 2 ? 6 : 5; }
 // (verify_down M = 2: 5 slices of 4 steps 14.2 us, 3 slices of 6 steps 15.2 us).
 __host__ __device__ constexpr int split_steps(int M) { return M == 1 ? 6 : 4; }
 constexpr int kShortSlice = 4;           // depth of the short no-refill form
-// Occupancy target (waves per SIMD).
-__host__ __device__ constexpr int waves_per_simd(int) { return 4; }
+// Occupancy target (waves per SIMD): M = 4's registers need the room of 3.
+__host__ __device__ constexpr int waves_per_simd(int M) { return M == 4 ? 3 : 4; }
 // Largest slice (blocks): whole steps, within the LDS budget and at most two
-// rings long (one at M = 3); and the (row, block) staging items per thread it
-// needs.
-__host__ __device__ constexpr int max_ring_rounds(int M) { return M == 3 ? 1 : 2; }   // M = 3's ring form would spill
+// rings long (one from M = 3 on); and the (row, block) staging items per
+// thread it needs.
+__host__ __device__ constexpr int max_ring_rounds(int M) { return M >= 3 ? 1 : 2; }   // the refilled form would spill
 __host__ __device__ constexpr int max_slice_blocks(int M) {
   return (kLdsBudget / (M * (4 * 16 + 4)) / kLanesPerRow) * kLanesPerRow <
                  max_ring_rounds(M) * ring_steps(M) * kLanesPerRow
@@ -441,6 +441,7 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t
     case 1: return launch_m<1>(x, codes, scales, y, N, K, p, ws, s);
     case 2: return launch_m<2>(x, codes, scales, y, N, K, p, ws, s);
     case 3: return launch_m<3>(x, codes, scales, y, N, K, p, ws, s);
+    case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -359,7 +359,7 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
 // what fits without spilling.
 template <int M, bool kScaleQuad>
 __global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kScaleQuad ? (stage_items(M) > 1 ? 5 : 6) : (M == 4 || stage_items(M) > 1 ? 4 : 5), 8)))
+__attribute__((amdgpu_waves_per_eu(kScaleQuad ? (stage_items(M) > 1 ? 5 : 6) : (stage_items(M) > 1 ? 4 : 5), 8)))
 mfma_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ codes,
                    const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
                    float* __restrict__ partial, uint32_t* __restrict__ counters,
@@ -855,7 +855,6 @@ hipError_t launch_skinny_mfma(const uint16_t* x, const uint8_t* codes, const uin
                               uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
                               void* ws, hipStream_t s) {
   switch (M) {
-    case 4: return launch_mfma_m<4>(x, codes, scales, y, N, K, p, ws, s);
     case 5: return launch_mfma_m<5>(x, codes, scales, y, N, K, p, ws, s);
     case 6: return launch_mfma_m<6>(x, codes, scales, y, N, K, p, ws, s);
     case 7: return launch_mfma_m<7>(x, codes, scales, y, N, K, p, ws, s);

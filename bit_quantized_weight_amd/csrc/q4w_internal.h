@@ -28,7 +28,7 @@ static_assert(int64_t(kCounterRegionBytes / 4) * kMinRowsPerTile >= kMaxSkinnyN,
               "one counter per row tile at the largest N");
 constexpr int kRouteDot2 = 0;     // VALU dot2 kernel (q4_gemv.hip)
 constexpr int kRouteMfma = 1;     // matrix-core kernel (q4_gemv_mfma.hip)
-constexpr int kMfmaMinM = 4;      // smallest M routed to the matrix cores
+constexpr int kMfmaMinM = 5;      // smallest M routed to the matrix cores
 struct SkinnyPlan {
   int route;           // kRouteDot2 or kRouteMfma
   int rows_per_wg;     // output rows per workgroup

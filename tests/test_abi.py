@@ -118,8 +118,8 @@ def test_gemv_split_policy(L):
         assert (b - region) % (m * n * 4) == 0, (m, n, k, b)
         return (b - region) // (m * n * 4)
 
-    # VALU kernel (M <= 3): one slice when a row fits the largest slice
-    # (12 steps at M = 1, 11 at M = 2 (LDS), 5 at M = 3) ...
+    # VALU kernel (M <= 4): one slice when a row fits the largest slice
+    # (12 steps at M = 1, 11 at M = 2 (LDS), 5 at M = 3 and 4) ...
     assert slices(1, 17408, 5120) == 1        # decode gate/up
     assert slices(1, 7168, 5120) == 1         # qkv
     assert slices(1, 5120, 5120) == 1         # out
@@ -133,11 +133,12 @@ def test_gemv_split_policy(L):
     assert slices(1, 5120, 17408) == 3        # verify down: 17 steps of 32 blocks
     assert slices(2, 5120, 17408) == 5
     assert slices(3, 5120, 17408) == 5
+    assert slices(4, 5120, 17408) == 5
     # ... and more slices only below 256 workgroups (16 rows each)
     assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
-    # matrix-core kernel (M >= 4): slices of at most 8 steps of 4 blocks, at
+    # matrix-core kernel (M >= 5): slices of at most 8 steps of 4 blocks, at
     # every width up to 16 (two activation staging items per thread past M = 8)
-    for m in (4, 5, 8, 9, 13, 16):
+    for m in (5, 8, 9, 13, 16):
         assert slices(m, 5120, 17408) == 17, m
     # ... and no more than that at or above 256 workgroups (64 rows each)
     assert slices(5, 5120, 5120) == 5          # 80 row tiles x 5 = 400 workgroups

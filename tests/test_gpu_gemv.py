@@ -236,12 +236,13 @@ def packed_sampled(n, k, seed, rows):
 
 
 @pytest.mark.parametrize("k", [992, 4064, 5088, 6112, 7136, 9184, 11232, 12256])
-@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_vector_kernel_slice_forms(m, k):
-    """Every form of the M <= 3 kernel on one slice per row tile (N = 4100:
+    """Every form of the M <= 4 kernel on one slice per row tile (N = 4100:
     257 tiles of 16 rows): 1 to 12 steps of 32 blocks, each step count with a
     ragged last step, covering the short no-refill form, the full-depth one,
-    the refilled ring and, at M = 3 past 5 steps, the split into slices."""
+    the refilled ring and, at M = 3 and 4 past 5 steps, the split into
+    slices."""
     n = 4100
     rows = tuple(np.unique(np.concatenate([[0, 15, 16, n - 1],
                                            np.random.default_rng(k).integers(0, n, 60)])).tolist())
