@@ -10,9 +10,10 @@ The timed region replays a HIP graph holding exactly K captured launches
 (launch-bound inner loops belong in graphs); the same K launches issued
 eagerly from Python are reported beside it.  Extra sections, each timed the
 same way, cover the rest of the path:
-  verify_down_per_M   K = 17408, N = 5120, M = 1..5 (speculative verify)
-  decode_step_64L     64 layers x {qkv, out, gate, up, down} at M = 5
-  a8w4_prefill        M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
+  verify_down_per_M      K = 17408, N = 5120, M = 1..16 (speculative verify)
+  decode_step_64L        64 layers x {qkv, out, gate, up, down} at M = 5
+  a8w4_prefill           M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
+  a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048 (section "pass")
 plus `roofline` for the dominant kernel and `cpu_baseline` (the oracle).
 """
 
@@ -290,7 +291,7 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sections", default="decode,verify,step,prefill",
+    ap.add_argument("--sections", default="decode,verify,step,prefill,pass",
                     help="comma list of extra sections (decode is always run)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
@@ -333,6 +334,7 @@ def main():
         extra["a8w4_prefill"] = bench_prefill(torch, q4w, synthetic, reps=20)
         log(f"[bench] a8w4_prefill: route {extra['a8w4_prefill']['ms_route']:.3f} ms "
             f"({extra['a8w4_prefill']['tok_s']:.0f} tok/s), GEMM {extra['a8w4_prefill']['ms_gemm']:.3f} ms")
+    if "pass" in sections:
         extra["a8w4_prefill_pass_64L"] = bench_prefill_pass(torch, q4w, synthetic, reps=3)
         for m_, r_ in extra["a8w4_prefill_pass_64L"]["per_M"].items():
             log(f"[bench] a8w4_prefill_pass_64L M={m_}: {r_['ms_graph']:.2f} ms ({r_['tok_s']:.0f} tok/s)")
