@@ -157,6 +157,25 @@ def test_act_quant_checks(L):
     assert q(p(A), 4, 64, p(A), p(A + 2), NUL) == ALIGN
 
 
+def test_a8_workspace_sizes(L):
+    """A8 workspace: quantized activations of M rounded up to 128 rows
+    (int8 [Mp, K], then fp32 scales [Mp, K/64], each 256-byte aligned), plus,
+    from 256 padded rows on, the GEMM's region for shared tiles: 512 arrival
+    counters (2 KiB) and two fp32 128 x 128 partial tiles per workgroup."""
+    f = L.a8w4_ws_bytes
+
+    def act(mp, k):
+        def a256(v):
+            return (v + 255) // 256 * 256
+        return a256(mp * k) + a256(mp * (k // 64) * 4)
+
+    region = 2048 + 2 * 512 * 128 * 128 * 4
+    assert f(1, 64) == act(128, 64)
+    assert f(128, 5120) == act(128, 5120)
+    assert f(129, 5120) == act(256, 5120) + region
+    assert f(2048, 17408) == act(2048, 17408) + region
+
+
 def test_a8_checks(L):
     gm = L.a8w4_gemm_prefill
     ws = L.a8w4_ws_bytes(64, 128)
