@@ -99,15 +99,16 @@ def test_tile_forms_block_sums_and_gemm(n):
     assert_close(host(y), a8.prefill(x, q, d), what=f"A8 M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("n", [38400, 38477])
-def test_chunk_balanced_form(n):
-    """M = 256, K = 256: 600 (or 602, with a ragged last column tile) tiles of
-    128 x 128 do not fill whole rounds of the 512 resident workgroups, so the
+@pytest.mark.parametrize("n,k", [(38400, 256), (38477, 256), (38400, 192)])
+def test_chunk_balanced_form(n, k):
+    """M = 256: 600 (or 602, with a ragged last column tile) tiles of 128 x 128
+    make more than one round of the 512 resident workgroups, so the
     chunk-balanced form runs: 512 equal ranges of 3 chunks (2 per tile), and
-    most tiles are summed by two workgroups.  Against the A8 oracle, and a
-    second call bit-identical to the first."""
+    most tiles are summed by two workgroups.  K = 192 has a half chunk at the
+    end of every tile.  Against the A8 oracle, and a second call
+    bit-identical to the first."""
     torch = torch_cuda()
-    m, k = 256, 256
+    m = 256
     codes, scales, q, d = _packed(n, k, 900 + n)
     x = synthetic.activations(m, k, 901)
     xd = dev(x, torch)
