@@ -92,8 +92,10 @@ def make_copies(torch, q4w, synthetic, n, k, base_seed):
     return copies
 
 
-def gemv_series(torch, q4w, copies, x, y, steps, warmup):
-    """Returns (graph seconds, eager seconds) for `steps` launches rotating over copies."""
+def gemv_series(torch, q4w, copies, x, y, steps, warmup, series=1):
+    """Returns (graph seconds, eager seconds) for `steps` launches rotating over
+    copies; with series > 1 the graph of `steps` launches is timed that many
+    times and the median is returned (and the list as a third value)."""
     m, k = x.shape
     n = copies[0][0].shape[0]
     ws = torch.zeros(max(q4w.gemv_ws_bytes(m, n, k, 0), 1), dtype=torch.uint8, device="cuda")
@@ -107,9 +109,11 @@ def gemv_series(torch, q4w, copies, x, y, steps, warmup):
     t_eager = time_region(torch, lambda: launches(steps))
     g = capture(torch, lambda: launches(steps))
     g.replay()
-    t_graph = time_region(torch, g.replay)
+    times = [time_region(torch, g.replay) for _ in range(series)]
     del g
-    return t_graph, t_eager
+    if series == 1:
+        return times[0], t_eager
+    return sorted(times)[series // 2], t_eager, times
 
 
 # --------------------------------------------------------------------------
@@ -139,12 +143,14 @@ def bench_verify(torch, q4w, synthetic, steps, warmup):
     copies = make_copies(torch, q4w, synthetic, n, k, 20_000)
     res = {}
     for m in (1, 2, 3, 4, 5, 8, 13, 16):      # 1..5: the verify workload; 8..16: wide drafts
+        # median of three timed graph replays of `steps` launches (min and max kept)
         x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-        tg, te = gemv_series(torch, q4w, copies, x, y, steps, warmup)
+        tg, te, ts = gemv_series(torch, q4w, copies, x, y, steps, warmup, series=3)
         b = gemv_bytes(m, k, n)
         res[str(m)] = dict(gbs_graph=b * steps / tg / 1e9, gbs_eager=b * steps / te / 1e9,
                            us_per_launch_graph=tg / steps * 1e6,
+                           us_per_launch_graph_min_max=[min(ts) / steps * 1e6, max(ts) / steps * 1e6],
                            frac_of_peak=b * steps / tg / 1e9 / HBM_PEAK_GBS)
     del copies
     torch.cuda.empty_cache()
