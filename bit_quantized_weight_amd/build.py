@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "lib")
 OUT = os.path.join(OUT_DIR, "libq4w.so")
 
-SOURCES = ["q4w_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemv_mfma.hip", "a8w4.hip"]
+SOURCES = ["q4w_api.cpp", "q4_pack.hip", "q4_gemv.hip", "q4_gemv_mfma.hip", "q4_gemv_mfma4.hip", "a8w4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

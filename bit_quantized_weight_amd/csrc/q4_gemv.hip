@@ -84,7 +84,7 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 // Rows per lane: more rows re-use the activation registers more (less LDS
 // traffic per weight) at the cost of registers and of fewer workgroups.
-// (This kernel serves M = 1..4; wider M goes to the matrix-core kernel.)
+// (This kernel serves M = 1..3; wider M goes to the matrix-core kernels.)
 __host__ __device__ constexpr int rows_per_lane(int) { return 2; }
 // Steps requested at once per wave (the register ring).
 __host__ __device__ constexpr int ring_steps(int M) { return M <= 2 ? 6 : 5; }
@@ -92,8 +92,8 @@ __host__ __device__ constexpr int ring_steps(int M) { return M <= 2 ? 6 : 5; }
 // (verify_down M = 2: 5 slices of 4 steps 14.2 us, 3 slices of 6 steps 15.2 us).
 __host__ __device__ constexpr int split_steps(int M) { return M == 1 ? 6 : 4; }
 constexpr int kShortSlice = 4;           // depth of the short no-refill form
-// Occupancy target (waves per SIMD): M = 4's registers need the room of 3.
-__host__ __device__ constexpr int waves_per_simd(int M) { return M == 4 ? 3 : 4; }
+// Occupancy target (waves per SIMD).
+__host__ __device__ constexpr int waves_per_simd(int) { return 4; }
 // Largest slice (blocks): whole steps, within the LDS budget and at most two
 // rings long (one from M = 3 on); and the (row, block) staging items per
 // thread it needs.
@@ -395,6 +395,7 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
 // the LDS budget needs more).
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   if (M >= kMfmaMinM) return plan_skinny_mfma(M, N, K, split_k);
+  if (M >= kMfma4MinM) return plan_skinny_mfma4(M, N, K, split_k);
   SkinnyPlan p{};
   p.route = kRouteDot2;
   p.rows_per_wg = kWaves * kSlots * rows_per_lane(M);
@@ -437,11 +438,11 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t
                          uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p, void* ws,
                          hipStream_t s) {
   if (p.route == kRouteMfma) return launch_skinny_mfma(x, codes, scales, y, M, N, K, p, ws, s);
+  if (p.route == kRouteMfma4) return launch_skinny_mfma4(x, codes, scales, y, M, N, K, p, ws, s);
   switch (M) {
     case 1: return launch_m<1>(x, codes, scales, y, N, K, p, ws, s);
     case 2: return launch_m<2>(x, codes, scales, y, N, K, p, ws, s);
     case 3: return launch_m<3>(x, codes, scales, y, N, K, p, ws, s);
-    case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

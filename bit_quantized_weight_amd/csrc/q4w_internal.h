@@ -27,10 +27,12 @@ constexpr int64_t kMaxSkinnyN = int64_t(1) << 19;
 static_assert(int64_t(kCounterRegionBytes / 4) * kMinRowsPerTile >= kMaxSkinnyN,
               "one counter per row tile at the largest N");
 constexpr int kRouteDot2 = 0;     // VALU dot2 kernel (q4_gemv.hip)
-constexpr int kRouteMfma = 1;     // matrix-core kernel (q4_gemv_mfma.hip)
-constexpr int kMfmaMinM = 5;      // smallest M routed to the matrix cores
+constexpr int kRouteMfma = 1;     // 16x16x32 matrix-core kernel (q4_gemv_mfma.hip)
+constexpr int kRouteMfma4 = 2;    // 4x4x4 matrix-core kernel (q4_gemv_mfma4.hip)
+constexpr int kMfmaMinM = 5;      // smallest M routed to the 16x16x32 kernel
+constexpr int kMfma4MinM = 4;     // M in [kMfma4MinM, kMfmaMinM) takes the 4x4x4 kernel
 struct SkinnyPlan {
-  int route;           // kRouteDot2 or kRouteMfma
+  int route;           // kRouteDot2, kRouteMfma or kRouteMfma4
   int rows_per_wg;     // output rows per workgroup
   int row_tiles;       // ceil(N / rows_per_wg)
   int splits;          // K slices
@@ -40,6 +42,10 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k);
 SkinnyPlan plan_skinny_mfma(int M, int64_t N, int64_t K, int split_k);
+SkinnyPlan plan_skinny_mfma4(int M, int64_t N, int64_t K, int split_k);
+hipError_t launch_skinny_mfma4(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                               uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
+                               void* ws, hipStream_t s);
 hipError_t launch_skinny_mfma(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
                               uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
                               void* ws, hipStream_t s);

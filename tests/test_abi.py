@@ -118,8 +118,9 @@ def test_gemv_split_policy(L):
         assert (b - region) % (m * n * 4) == 0, (m, n, k, b)
         return (b - region) // (m * n * 4)
 
-    # VALU kernel (M <= 4): one slice when a row fits the largest slice
-    # (12 steps at M = 1, 11 at M = 2 (LDS), 5 at M = 3 and 4) ...
+    # VALU kernel (M <= 3): one slice when a row fits the largest slice
+    # (12 steps of 32 blocks at M = 1, 11 at M = 2 (LDS), 5 at M = 3); the
+    # 4x4x4 kernel (M = 4): 10 steps of 16 blocks, else slices of 8 at most ...
     assert slices(1, 17408, 5120) == 1        # decode gate/up
     assert slices(1, 7168, 5120) == 1         # qkv
     assert slices(1, 5120, 5120) == 1         # out

@@ -238,11 +238,13 @@ def packed_sampled(n, k, seed, rows):
 @pytest.mark.parametrize("k", [992, 4064, 5088, 6112, 7136, 9184, 11232, 12256])
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 def test_vector_kernel_slice_forms(m, k):
-    """Every form of the M <= 4 kernel on one slice per row tile (N = 4100:
-    257 tiles of 16 rows): 1 to 12 steps of 32 blocks, each step count with a
-    ragged last step, covering the short no-refill form, the full-depth one,
-    the refilled ring and, at M = 3 and 4 past 5 steps, the split into
-    slices."""
+    """Every form of the M <= 4 kernels on one slice per row tile (N = 4100:
+    257 tiles of 16 rows): K from 31 to 383 blocks, each with a ragged last
+    step.  M <= 3 (the v_dot2 kernel, 32-block steps): the short no-refill
+    form, the full-depth one, the refilled ring and, at M = 3 past 5 steps,
+    the split into slices.  M = 4 (the 4x4x4 kernel, 16-block steps): every
+    depth up to 10 steps with one 4-row group per wave, and past 10 steps the
+    split into slices with two groups per wave."""
     n = 4100
     rows = tuple(np.unique(np.concatenate([[0, 15, 16, n - 1],
                                            np.random.default_rng(k).integers(0, n, 60)])).tolist())
