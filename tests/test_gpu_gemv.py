@@ -45,12 +45,15 @@ def test_shapes_and_ragged_tails(m, n, k):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
-def test_explicit_split_k(split):
+@pytest.mark.parametrize("m", [3, 4])
+def test_explicit_split_k(m, split):
+    """The v_dot2 kernel (M = 3) and the 4x4x4 kernel (M = 4) with a forced
+    slice count, over a ragged last row tile (N = 200)."""
     codes, scales, q, d = packed(200, 2048, 30)
-    x = synthetic.activations(3, 2048, 31)
+    x = synthetic.activations(m, 2048, 31)
     ref = q4.matmul(x, q, d)
     y1 = run(x, codes, scales, split)
-    assert_close(y1, ref, what=f"split={split}")
+    assert_close(y1, ref, what=f"M={m} split={split}")
     y2 = run(x, codes, scales, split)
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
@@ -92,16 +95,18 @@ def test_workspace_shared_across_shapes():
         assert_close(host(yb), q4.matmul(xb, qb, db), what="shape B")
 
 
-def test_one_hot_bit_exact():
-    """x = e_k gives fp16(q[n,k] * d[n,k//32]): one product, rounded once."""
+@pytest.mark.parametrize("m", [4, 8])
+def test_one_hot_bit_exact(m):
+    """x = e_k gives fp16(q[n,k] * d[n,k//32]): one product, rounded once
+    (M = 4: the 4x4x4 kernel; M = 8: the 16x16x32 kernel)."""
     n, k = 96, 256
     codes, scales, q, d = packed(n, k, 40)
-    for start in range(0, k, 8):
-        x = np.zeros((8, k), np.float16)
-        for r in range(8):
+    for start in range(0, k, m):
+        x = np.zeros((m, k), np.float16)
+        for r in range(m):
             x[r, start + r] = 1.0
         y = run(x, codes, scales)
-        for r in range(8):
+        for r in range(m):
             kk = start + r
             want = (q[:, kk].astype(np.float64) * d[:, kk // 32].astype(np.float64)).astype(np.float16)
             assert np.array_equal(y[r], want), kk
@@ -143,7 +148,7 @@ def test_invariants_bit_exact():
     only: the hardware fp16 dot product does not round symmetrically in sign,
     so negation can move a result by one fp16 ulp."""
     codes, scales, q, d = packed(5120, 17408, synthetic.WEIGHT_SEED)
-    for m in (2, 4):          # one width per route (VALU dot2 and matrix cores)
+    for m in (2, 4, 5):       # one width per route (v_dot2, 4x4x4 and 16x16x32 kernels)
         x = synthetic.activations(m, 17408, 50)
         y = run(x, codes, scales)
         y2 = run((x.astype(np.float32) * 2).astype(np.float16), codes, scales)
@@ -202,10 +207,11 @@ def test_empty_shapes():
     assert y.shape == (1, 0)
 
 
-@pytest.mark.parametrize("m", [1, 5])
+@pytest.mark.parametrize("m", [1, 4, 5])
 def test_large_n_split_counters(m):
-    """N just under 2^19 with split-K: 65,535 row tiles of 8 rows at M = 1, so
-    the arrival counters span the whole counter region.  Sampled rows,
+    """N just under 2^19 with split-K: 65,535 row tiles of 8 rows at M = 1
+    (16,384 of 32 rows at M = 4), so the arrival counters span the whole
+    counter region at M = 1.  Sampled rows,
     including both ends, are checked against the oracle."""
     torch = torch_cuda()
     n, k = (1 << 19) - 8, 2048
