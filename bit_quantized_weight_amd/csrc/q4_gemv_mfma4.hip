@@ -40,6 +40,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStepBlocks = 16;            // 32-weight blocks per step (one per lane group)
 constexpr int kFixupBatch = 16;
 constexpr int kMaxSliceSteps = 10;         // the deepest copy of the kernel
+constexpr int kSplitSliceSteps = 4;        // longest slice of a split row
+constexpr int kWideTileMinWgs = 512;       // 64-row tiles only with this many workgroups
 constexpr int kMinWgs = 256;               // one workgroup per CU
 constexpr int kCachePolicyNT = 2;          // non-temporal: codes are read once, in whole lines
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -302,6 +304,10 @@ hipError_t launch_mr(const uint16_t* x, const uint8_t* codes, const uint16_t* sc
 template <int M>
 hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
                     int64_t N, int64_t K, const SkinnyPlan& p, void* ws, hipStream_t s) {
+  if (p.rows_per_wg == 16 * kWaves) {   // four row groups: built for short slices only
+    if ((p.blocks_per_split + kStepBlocks - 1) / kStepBlocks > kSplitSliceSteps) return hipErrorInvalidValue;
+    return launch_p<M, kSplitSliceSteps, 4>(x, codes, scales, y, N, K, p, ws, s);
+  }
   if (p.rows_per_wg == 8 * kWaves) return launch_mr<M, 2>(x, codes, scales, y, N, K, p, ws, s);
   return launch_mr<M, 1>(x, codes, scales, y, N, K, p, ws, s);
 }
@@ -309,27 +315,35 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
 }  // namespace
 
 // Split plan: one slice when a row fits the deepest copy (10 steps of 16
-// blocks), else slices of at most 8 steps; more slices only below kMinWgs
-// workgroups.  split_k > 0 asks for that many slices (raised when a slice
-// would be longer than the deepest copy).
+// blocks), else slices of at most 4 steps, on 64-row tiles when that still
+// gives kWideTileMinWgs workgroups and on 32-row tiles otherwise; more slices
+// only below kMinWgs workgroups.  split_k > 0 asks for that many slices
+// (raised when a slice would be longer than the deepest copy) on 32-row tiles.
 SkinnyPlan plan_skinny_mfma4(int M, int64_t N, int64_t K, int split_k) {
   SkinnyPlan p{};
   p.route = kRouteMfma4;
   const int nb = (int)(K / kBlock);
   const int steps_total = (nb + kStepBlocks - 1) / kStepBlocks;
-  // Two 4-row groups per wave (32-row tiles) when K is split, one otherwise
-  // (measured at M = 4: verify_down 17.62 -> 17.33 us with two groups, while
-  // the one-slice shapes, gate/up, qkv and out, lose 0.5-1 us with them).
+  // One 4-row group per wave (16-row tiles) on one-slice rows; when K is
+  // split, four groups (64-row tiles) if there are enough workgroups, else
+  // two.  Measured at M = 4, K = 17408 (us): N = 5120 17.39 with slices of 8
+  // steps on 32-row tiles, 15.31 with slices of 4, 15.16 with slices of 4 on
+  // 64-row tiles (720 workgroups); N = 8192 21.91, 21.37, 20.24; N = 2560
+  // (360 workgroups on 64-row tiles) 11.23, 10.00, 10.88.  The one-slice
+  // shapes (K = 5120) measured no better split.
   const bool split = split_k > 1 || (split_k <= 0 && steps_total > kMaxSliceSteps);
-  p.rows_per_wg = (split ? 8 : 4) * kWaves;
-  p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
-  int S;
+  int S = 1;
+  int groups = split ? 2 : 1;
   if (split_k > 0) {
     S = split_k;
-  } else {
-    S = steps_total <= kMaxSliceSteps ? 1 : (steps_total + 7) / 8;
-    while ((int64_t)S * p.row_tiles < kMinWgs && steps_total / (S + 1) >= 1) ++S;
+  } else if (split) {
+    S = (steps_total + kSplitSliceSteps - 1) / kSplitSliceSteps;
+    if ((N + 16 * kWaves - 1) / (16 * kWaves) * S >= kWideTileMinWgs) groups = 4;
   }
+  p.rows_per_wg = 4 * groups * kWaves;
+  p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
+  if (split_k <= 0)
+    while ((int64_t)S * p.row_tiles < kMinWgs && steps_total / (S + 1) >= 1) ++S;
   if (S < 1) S = 1;
   int sps = (steps_total + S - 1) / S;                 // steps per slice
   if (sps > kMaxSliceSteps) sps = kMaxSliceSteps;

@@ -120,7 +120,7 @@ def test_gemv_split_policy(L):
 
     # VALU kernel (M <= 3): one slice when a row fits the largest slice
     # (12 steps of 32 blocks at M = 1, 11 at M = 2 (LDS), 5 at M = 3); the
-    # 4x4x4 kernel (M = 4): 10 steps of 16 blocks, else slices of 8 at most ...
+    # 4x4x4 kernel (M = 4): 10 steps of 16 blocks, else slices of 4 at most ...
     assert slices(1, 17408, 5120) == 1        # decode gate/up
     assert slices(1, 7168, 5120) == 1         # qkv
     assert slices(1, 5120, 5120) == 1         # out
@@ -134,7 +134,9 @@ def test_gemv_split_policy(L):
     assert slices(1, 5120, 17408) == 3        # verify down: 17 steps of 32 blocks
     assert slices(2, 5120, 17408) == 5
     assert slices(3, 5120, 17408) == 5
-    assert slices(4, 5120, 17408) == 5
+    assert slices(4, 5120, 17408) == 9        # 34 steps of 16 blocks: slices of 4
+    assert slices(4, 4100, 11232) == 6        # 22 steps
+    assert slices(4, 4100, 5120) == 1         # 10 steps: one slice
     # ... and more slices only below 256 workgroups (16 rows each)
     assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
     # matrix-core kernel (M >= 5): slices of at most 8 steps of 4 blocks, at

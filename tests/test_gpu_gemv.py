@@ -130,6 +130,22 @@ def test_decode_gate_up():
     assert_close(run(x, codes, scales), q4.matmul(x, q, d), what="decode_gate_up")
 
 
+@pytest.mark.parametrize("n,k", [(5000, 17408), (2560, 17408 - 32), (8192, 8192 + 32)])
+def test_split_row_tiles_m4(n, k):
+    """The 4x4x4 kernel's split forms at M = 4: 64-row tiles (N = 5000, 711
+    workgroups: 79 tiles, the last one ragged, x 9 slices of 4 steps;
+    N = 8192, K = 8224) and 32-row tiles (N = 2560, where 64-row tiles would
+    give only 360 workgroups), each over a ragged last step where K is not a
+    multiple of 512.  Sampled rows include both ends."""
+    rows = tuple(np.unique(np.concatenate([[0, 63, 64, n - 65, n - 1],
+                                           np.random.default_rng(n).integers(0, n, 60)])).tolist())
+    codes, scales, q, d = packed_sampled(n, k, 92, rows)
+    x = synthetic.activations(4, k, 93)
+    y = run(x, codes, scales)
+    assert_close(y[:, list(rows)], q4.matmul(x, q, d), what=f"M=4 K={k} N={n}")
+    assert np.array_equal(run(x, codes, scales).view(np.uint16), y.view(np.uint16))
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5])
 def test_verify_down(m):
     """Speculative verify, down-projection shape: K = 17408, N = 5120, M = 1..5."""
