@@ -396,6 +396,12 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
 SkinnyPlan plan_skinny(int M, int64_t N, int64_t K, int split_k) {
   if (M >= kMfmaMinM) return plan_skinny_mfma(M, N, K, split_k);
   if (M >= kMfma4MinM) return plan_skinny_mfma4(M, N, K, split_k);
+  // At M = 3 the 4x4x4 kernel's short split slices beat this kernel's on
+  // rows that need splitting (K = 17408, N = 5120: 15.31 -> 14.58 us); on
+  // one-slice rows this kernel stays ahead (K = 5120, N = 7168: 7.42 against
+  // 7.67 us), and at M = 2 it does on both (13.74 against 13.98 us).
+  if (M == kMfma4SplitM && split_k <= 0 && K / kBlock > kMfma4SliceBlocks)
+    return plan_skinny_mfma4(M, N, K, split_k);
   SkinnyPlan p{};
   p.route = kRouteDot2;
   p.rows_per_wg = kWaves * kSlots * rows_per_lane(M);

@@ -40,6 +40,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kStepBlocks = 16;            // 32-weight blocks per step (one per lane group)
 constexpr int kFixupBatch = 16;
 constexpr int kMaxSliceSteps = 10;         // the deepest copy of the kernel
+static_assert(kMaxSliceSteps * kStepBlocks == kMfma4SliceBlocks, "one-slice rows");
 constexpr int kSplitSliceSteps = 4;        // longest slice of a split row
 constexpr int kWideTileMinWgs = 512;       // 64-row tiles only with this many workgroups
 constexpr int kMinWgs = 256;               // one workgroup per CU
@@ -361,6 +362,7 @@ hipError_t launch_skinny_mfma4(const uint16_t* x, const uint8_t* codes, const ui
                                uint16_t* y, int M, int64_t N, int64_t K, const SkinnyPlan& p,
                                void* ws, hipStream_t s) {
   switch (M) {
+    case 3: return launch_m<3>(x, codes, scales, y, N, K, p, ws, s);
     case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }

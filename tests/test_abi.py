@@ -129,11 +129,11 @@ def test_gemv_split_policy(L):
     assert slices(2, 4100, 11232) == 1        # 11 steps
     assert slices(2, 4100, 12256) == 3        # 12 steps: slices of 4
     assert slices(3, 4100, 5088) == 1         # 5 steps
-    assert slices(3, 4100, 6112) == 2         # 6 steps: slices of 4
+    assert slices(3, 4100, 6112) == 3         # 191 blocks: past one slice, M = 3 takes the 4x4x4 kernel
     # ... else slices of 6 steps at M = 1, 4 above (within the ring: no refill)
     assert slices(1, 5120, 17408) == 3        # verify down: 17 steps of 32 blocks
     assert slices(2, 5120, 17408) == 5
-    assert slices(3, 5120, 17408) == 5
+    assert slices(3, 5120, 17408) == 9        # the 4x4x4 kernel, as at M = 4
     assert slices(4, 5120, 17408) == 9        # 34 steps of 16 blocks: slices of 4
     assert slices(4, 4100, 11232) == 6        # 22 steps
     assert slices(4, 4100, 5120) == 1         # 10 steps: one slice

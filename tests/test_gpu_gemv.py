@@ -131,8 +131,9 @@ def test_decode_gate_up():
 
 
 @pytest.mark.parametrize("n,k", [(5000, 17408), (2560, 17408 - 32), (8192, 8192 + 32)])
-def test_split_row_tiles_m4(n, k):
-    """The 4x4x4 kernel's split forms at M = 4: 64-row tiles (N = 5000, 711
+@pytest.mark.parametrize("m", [3, 4])
+def test_split_row_tiles_4x4x4(m, n, k):
+    """The 4x4x4 kernel's split forms at M = 3 and 4: 64-row tiles (N = 5000, 711
     workgroups: 79 tiles, the last one ragged, x 9 slices of 4 steps;
     N = 8192, K = 8224) and 32-row tiles (N = 2560, where 64-row tiles would
     give only 360 workgroups), each over a ragged last step where K is not a
@@ -140,9 +141,9 @@ def test_split_row_tiles_m4(n, k):
     rows = tuple(np.unique(np.concatenate([[0, 63, 64, n - 65, n - 1],
                                            np.random.default_rng(n).integers(0, n, 60)])).tolist())
     codes, scales, q, d = packed_sampled(n, k, 92, rows)
-    x = synthetic.activations(4, k, 93)
+    x = synthetic.activations(m, k, 93)
     y = run(x, codes, scales)
-    assert_close(y[:, list(rows)], q4.matmul(x, q, d), what=f"M=4 K={k} N={n}")
+    assert_close(y[:, list(rows)], q4.matmul(x, q, d), what=f"M={m} K={k} N={n}")
     assert np.array_equal(run(x, codes, scales).view(np.uint16), y.view(np.uint16))
 
 
@@ -263,10 +264,10 @@ def test_vector_kernel_slice_forms(m, k):
     """Every form of the M <= 4 kernels on one slice per row tile (N = 4100:
     257 tiles of 16 rows): K from 31 to 383 blocks, each with a ragged last
     step.  M <= 3 (the v_dot2 kernel, 32-block steps): the short no-refill
-    form, the full-depth one, the refilled ring and, at M = 3 past 5 steps,
-    the split into slices.  M = 4 (the 4x4x4 kernel, 16-block steps): every
-    depth up to 10 steps with one 4-row group per wave, and past 10 steps the
-    split into slices with two groups per wave."""
+    form, the full-depth one and the refilled ring.  M = 4 (the 4x4x4
+    kernel, 16-block steps): every depth up to 10 steps with one 4-row group
+    per wave, and past 10 steps the split into slices with two groups per
+    wave; M = 3 takes the same split form past 160 blocks."""
     n = 4100
     rows = tuple(np.unique(np.concatenate([[0, 15, 16, n - 1],
                                            np.random.default_rng(k).integers(0, n, 60)])).tolist())
