@@ -1,4 +1,5 @@
-// q4_gemv_skinny at M = 4 on 4 x 4 x 4 matrix-core blocks.
+// q4_gemv_skinny at M = 4..6 (and M = 3 rows that need splitting) on
+// 4 x 4 x 4 matrix-core blocks.
 //
 // Same operation and pages as q4_gemv.hip: decode and speculative verify
 // stream every quantized weight once per step (page 3, "Qwen3.8-27B at 256K
@@ -10,8 +11,9 @@
 //    b of the instruction is lanes 4b..4b+3; lane 4b + i supplies row i of A
 //    and column i of B and receives column i of D (rows 0..3).  Here A is the
 //    (up to 4) activation rows and B four weight rows, so no operand row is
-//    padding beyond M <= 4, and the v_dot2 form's M dot products per weight
-//    pair become one matrix instruction per 4 x 4 x 4 product.
+//    padding at M = 4, and the v_dot2 form's M dot products per weight
+//    pair become one matrix instruction per 4 x 4 x 4 product.  M = 5, 6
+//    take a second A operand (rows 4..7) against the same unpacked B.
 //  * Lane 4b + i of a wave owns weight rows 8w + i and 8w + 4 + i of its
 //    workgroup tile (two 4-row groups that share the A operand) and 32-weight
 //    block b of every 16-block step, so one 128-bit load of a wave reads 4
@@ -84,7 +86,9 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
                     const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
                     float* __restrict__ partial, uint32_t* __restrict__ counters, int N, int K,
                     int bps, int S) {
-  static_assert(M >= 1 && M <= 4, "one 4-row A operand");
+  static_assert(M >= 1 && M <= 8, "one or two 4-row A operands");
+  constexpr int kASets = (M + 3) / 4;        // A operands: activation rows 4j..4j+3
+  constexpr int MP = 4 * kASets;             // bias entries per block
   constexpr int kRowsPerWg = 4 * kRowGroups * kWaves;
   extern __shared__ uint4 smem[];
 
@@ -157,7 +161,7 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
     }
   }
 
-  // ---- stage: xs[q][b][m] (16 bytes each), bias[b][4] ------------------------
+  // ---- stage: xs[q][b][m] (16 bytes each), bias[b][MP] -----------------------
   // (m fastest, then b: the 64 lanes of an operand read, lane 4 blk + c, touch
   // one contiguous run of 16-byte entries, so the LDS reads are conflict-free)
   uint4* xs = smem;
@@ -186,15 +190,16 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
         s = dot2(o.z, k1032, s);
         s = dot2(o.w, k72, s);
       }
-      bias[b * 4 + m] = -s;
+      bias[b * MP + m] = -s;
     }
   }
   __syncthreads();
 
   // A rows past M read row 0 (their products land in D rows that are dropped).
-  const int arow = c < M ? c : 0;
-  const uint4* xa = xs + blk * M + arow;             // + word q: q * bpad * M; + step t: t * kStepBlocks * M
-  const float* ba = bias + blk * 4;                  // + step t: t * kStepBlocks * 4
+  const uint4* xa[kASets];                           // + word q: q * bpad * M; + step t: t * kStepBlocks * M
+#pragma unroll
+  for (int j = 0; j < kASets; ++j) xa[j] = xs + blk * M + (4 * j + c < M ? 4 * j + c : 0);
+  const float* ba = bias + blk * MP;                 // + step t: t * kStepBlocks * MP
 
   float yacc[kRowGroups][M];
 #pragma unroll
@@ -204,15 +209,19 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
 #pragma unroll
   for (int t = 0; t < P; ++t) {
     if (t < steps) {
-      const float* bt = ba + t * kStepBlocks * 4;
-      const f4 nb4 = f4{bt[0], bt[1], bt[2], bt[3]};   // -bias of rows 0..3
-      f4 d[kRowGroups];
+      const float* bt = ba + t * kStepBlocks * MP;
+      f4 d[kRowGroups][kASets];
 #pragma unroll
-      for (int r = 0; r < kRowGroups; ++r) d[r] = nb4;
-      const uint4* at = xa + t * kStepBlocks * M;
+      for (int j = 0; j < kASets; ++j) {
+        const f4 nb4 = f4{bt[4 * j], bt[4 * j + 1], bt[4 * j + 2], bt[4 * j + 3]};   // -bias, rows 4j..4j+3
+#pragma unroll
+        for (int r = 0; r < kRowGroups; ++r) d[r][j] = nb4;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint4 a = at[q * bpad * M];
+        uint4 a[kASets];
+#pragma unroll
+        for (int j = 0; j < kASets; ++j) a[j] = xa[j][t * kStepBlocks * M + q * bpad * M];
 #pragma unroll
         for (int r = 0; r < kRowGroups; ++r) {
           const uint32_t w = word(cw[t][r], q);
@@ -221,15 +230,18 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
           const uint32_t p1 = (w & 0x00F000F0u) ^ 0x54805480u;   // 64 + u, nibbles 1, 5
           const uint32_t p2 = (w8 & 0x000F000Fu) ^ 0x64086408u;  // nibbles 2, 6
           const uint32_t p3 = (w8 & 0x00F000F0u) ^ 0x54805480u;  // nibbles 3, 7
-          d[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(halves(a.x, a.y), halves(p0, p1), d[r], 0, 0, 0);
-          d[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(halves(a.z, a.w), halves(p2, p3), d[r], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < kASets; ++j) {
+            d[r][j] = __builtin_amdgcn_mfma_f32_4x4x4f16(halves(a[j].x, a[j].y), halves(p0, p1), d[r][j], 0, 0, 0);
+            d[r][j] = __builtin_amdgcn_mfma_f32_4x4x4f16(halves(a[j].z, a[j].w), halves(p2, p3), d[r][j], 0, 0, 0);
+          }
         }
       }
 #pragma unroll
       for (int r = 0; r < kRowGroups; ++r) {
         const float s = __half2float(__ushort_as_half((unsigned short)sw[t][r]));
 #pragma unroll
-        for (int m = 0; m < M; ++m) yacc[r][m] = fmaf(d[r][m], s, yacc[r][m]);
+        for (int m = 0; m < M; ++m) yacc[r][m] = fmaf(d[r][m / 4][m % 4], s, yacc[r][m]);
       }
     }
   }
@@ -278,7 +290,7 @@ template <int M, int P, int R>
 hipError_t launch_p(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
                     int64_t N, int64_t K, const SkinnyPlan& p, void* ws, hipStream_t s) {
   const int bpad = ((p.blocks_per_split + kStepBlocks - 1) / kStepBlocks) * kStepBlocks;
-  const size_t lds = (size_t)bpad * (M * 4 * sizeof(uint4) + 4 * sizeof(float));
+  const size_t lds = (size_t)bpad * (M * 4 * sizeof(uint4) + 4 * ((M + 3) / 4) * sizeof(float));
   uint32_t* counters = nullptr;
   float* partial = nullptr;
   if (p.splits > 1) {
@@ -305,9 +317,12 @@ hipError_t launch_mr(const uint16_t* x, const uint8_t* codes, const uint16_t* sc
 template <int M>
 hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
                     int64_t N, int64_t K, const SkinnyPlan& p, void* ws, hipStream_t s) {
-  if (p.rows_per_wg == 16 * kWaves) {   // four row groups: built for short slices only
-    if ((p.blocks_per_split + kStepBlocks - 1) / kStepBlocks > kSplitSliceSteps) return hipErrorInvalidValue;
-    return launch_p<M, kSplitSliceSteps, 4>(x, codes, scales, y, N, K, p, ws, s);
+  if (p.rows_per_wg == 16 * kWaves) {   // four row groups: built for short slices and M <= 4 only
+    if constexpr (M <= 4) {
+      if ((p.blocks_per_split + kStepBlocks - 1) / kStepBlocks <= kSplitSliceSteps)
+        return launch_p<M, kSplitSliceSteps, 4>(x, codes, scales, y, N, K, p, ws, s);
+    }
+    return hipErrorInvalidValue;
   }
   if (p.rows_per_wg == 8 * kWaves) return launch_mr<M, 2>(x, codes, scales, y, N, K, p, ws, s);
   return launch_mr<M, 1>(x, codes, scales, y, N, K, p, ws, s);
@@ -331,15 +346,18 @@ SkinnyPlan plan_skinny_mfma4(int M, int64_t N, int64_t K, int split_k) {
   // steps on 32-row tiles, 15.31 with slices of 4, 15.16 with slices of 4 on
   // 64-row tiles (720 workgroups); N = 8192 21.91, 21.37, 20.24; N = 2560
   // (360 workgroups on 64-row tiles) 11.23, 10.00, 10.88.  The one-slice
-  // shapes (K = 5120) measured no better split.
-  const bool split = split_k > 1 || (split_k <= 0 && steps_total > kMaxSliceSteps);
+  // shapes (K = 5120) measured no better split at M = 4.  With two A
+  // operands (M = 5, 6) rows of more than 4 steps are split too (M = 5,
+  // K = 5120, us: N = 17408 20.95 -> 17.15, N = 7168 10.49 -> 9.98).
+  const int one_slice_steps = M > 4 ? kSplitSliceSteps : kMaxSliceSteps;
+  const bool split = split_k > 1 || (split_k <= 0 && steps_total > one_slice_steps);
   int S = 1;
   int groups = split ? 2 : 1;
   if (split_k > 0) {
     S = split_k;
   } else if (split) {
     S = (steps_total + kSplitSliceSteps - 1) / kSplitSliceSteps;
-    if ((N + 16 * kWaves - 1) / (16 * kWaves) * S >= kWideTileMinWgs) groups = 4;
+    if (M <= 4 && (N + 16 * kWaves - 1) / (16 * kWaves) * S >= kWideTileMinWgs) groups = 4;
   }
   p.rows_per_wg = 4 * groups * kWaves;
   p.row_tiles = (int)((N + p.rows_per_wg - 1) / p.rows_per_wg);
@@ -364,6 +382,8 @@ hipError_t launch_skinny_mfma4(const uint16_t* x, const uint8_t* codes, const ui
   switch (M) {
     case 3: return launch_m<3>(x, codes, scales, y, N, K, p, ws, s);
     case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
+    case 5: return launch_m<5>(x, codes, scales, y, N, K, p, ws, s);
+    case 6: return launch_m<6>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

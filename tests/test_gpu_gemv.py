@@ -45,10 +45,11 @@ def test_shapes_and_ragged_tails(m, n, k):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
-@pytest.mark.parametrize("m", [3, 4])
+@pytest.mark.parametrize("m", [3, 4, 6])
 def test_explicit_split_k(m, split):
-    """The v_dot2 kernel (M = 3) and the 4x4x4 kernel (M = 4) with a forced
-    slice count, over a ragged last row tile (N = 200)."""
+    """The v_dot2 kernel (M = 3) and the 4x4x4 kernel with one (M = 4) and two
+    (M = 6) A operands with a forced slice count, over a ragged last row tile
+    (N = 200)."""
     codes, scales, q, d = packed(200, 2048, 30)
     x = synthetic.activations(m, 2048, 31)
     ref = q4.matmul(x, q, d)
@@ -58,11 +59,11 @@ def test_explicit_split_k(m, split):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
 
-@pytest.mark.parametrize("m", [5, 13])
+@pytest.mark.parametrize("m", [7, 13])
 def test_explicit_split_k_matrix_core(m):
-    """Matrix-core kernel with many slices (K = 4096, split_k = 64 gives 32
+    """16x16x32 kernel with many slices (K = 4096, split_k = 64 gives 32
     one-step slices): the fixup's partial loads go out in several chunks
-    (18 slices per chunk at M = 5, 9 at M = 13), over a ragged last row tile."""
+    (18 slices per chunk at M = 7, 9 at M = 13), over a ragged last row tile."""
     codes, scales, q, d = packed(300, 4096, 40)
     x = synthetic.activations(m, 4096, 41 + m)
     ref = q4.matmul(x, q, d)
@@ -95,18 +96,20 @@ def test_workspace_shared_across_shapes():
         assert_close(host(yb), q4.matmul(xb, qb, db), what="shape B")
 
 
-@pytest.mark.parametrize("m", [4, 8])
+@pytest.mark.parametrize("m", [4, 6, 8])
 def test_one_hot_bit_exact(m):
     """x = e_k gives fp16(q[n,k] * d[n,k//32]): one product, rounded once
-    (M = 4: the 4x4x4 kernel; M = 8: the 16x16x32 kernel)."""
+    (M = 4, 6: the 4x4x4 kernel with one and two A operands; M = 8: the
+    16x16x32 kernel)."""
     n, k = 96, 256
     codes, scales, q, d = packed(n, k, 40)
     for start in range(0, k, m):
+        live = [r for r in range(m) if start + r < k]
         x = np.zeros((m, k), np.float16)
-        for r in range(m):
+        for r in live:
             x[r, start + r] = 1.0
         y = run(x, codes, scales)
-        for r in range(m):
+        for r in live:
             kk = start + r
             want = (q[:, kk].astype(np.float64) * d[:, kk // 32].astype(np.float64)).astype(np.float16)
             assert np.array_equal(y[r], want), kk
@@ -165,7 +168,7 @@ def test_invariants_bit_exact():
     only: the hardware fp16 dot product does not round symmetrically in sign,
     so negation can move a result by one fp16 ulp."""
     codes, scales, q, d = packed(5120, 17408, synthetic.WEIGHT_SEED)
-    for m in (2, 4, 5):       # one width per route (v_dot2, 4x4x4 and 16x16x32 kernels)
+    for m in (2, 4, 6, 8):    # v_dot2, 4x4x4 (one and two A operands), 16x16x32
         x = synthetic.activations(m, 17408, 50)
         y = run(x, codes, scales)
         y2 = run((x.astype(np.float32) * 2).astype(np.float16), codes, scales)
@@ -224,7 +227,7 @@ def test_empty_shapes():
     assert y.shape == (1, 0)
 
 
-@pytest.mark.parametrize("m", [1, 4, 5])
+@pytest.mark.parametrize("m", [1, 4, 8])
 def test_large_n_split_counters(m):
     """N just under 2^19 with split-K: 65,535 row tiles of 8 rows at M = 1
     (16,384 of 32 rows at M = 4), so the arrival counters span the whole
