@@ -1,4 +1,4 @@
-// q4_gemv_skinny at M = 4..6 (and M = 3 rows that need splitting) on
+// q4_gemv_skinny at M = 4..7 (and M = 3 rows that need splitting) on
 // 4 x 4 x 4 matrix-core blocks.
 //
 // Same operation and pages as q4_gemv.hip: decode and speculative verify
@@ -12,7 +12,7 @@
 //    and column i of B and receives column i of D (rows 0..3).  Here A is the
 //    (up to 4) activation rows and B four weight rows, so no operand row is
 //    padding at M = 4, and the v_dot2 form's M dot products per weight
-//    pair become one matrix instruction per 4 x 4 x 4 product.  M = 5, 6
+//    pair become one matrix instruction per 4 x 4 x 4 product.  M = 5..7
 //    take a second A operand (rows 4..7) against the same unpacked B.
 //  * Lane 4b + i of a wave owns weight rows 8w + i and 8w + 4 + i of its
 //    workgroup tile (two 4-row groups that share the A operand) and 32-weight
@@ -347,7 +347,7 @@ SkinnyPlan plan_skinny_mfma4(int M, int64_t N, int64_t K, int split_k) {
   // 64-row tiles (720 workgroups); N = 8192 21.91, 21.37, 20.24; N = 2560
   // (360 workgroups on 64-row tiles) 11.23, 10.00, 10.88.  The one-slice
   // shapes (K = 5120) measured no better split at M = 4.  With two A
-  // operands (M = 5, 6) rows of more than 4 steps are split too (M = 5,
+  // operands (M = 5..7) rows of more than 4 steps are split too (M = 5,
   // K = 5120, us: N = 17408 20.95 -> 17.15, N = 7168 10.49 -> 9.98).
   const int one_slice_steps = M > 4 ? kSplitSliceSteps : kMaxSliceSteps;
   const bool split = split_k > 1 || (split_k <= 0 && steps_total > one_slice_steps);
@@ -384,6 +384,7 @@ hipError_t launch_skinny_mfma4(const uint16_t* x, const uint8_t* codes, const ui
     case 4: return launch_m<4>(x, codes, scales, y, N, K, p, ws, s);
     case 5: return launch_m<5>(x, codes, scales, y, N, K, p, ws, s);
     case 6: return launch_m<6>(x, codes, scales, y, N, K, p, ws, s);
+    case 7: return launch_m<7>(x, codes, scales, y, N, K, p, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

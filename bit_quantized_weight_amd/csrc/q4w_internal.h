@@ -29,7 +29,7 @@ static_assert(int64_t(kCounterRegionBytes / 4) * kMinRowsPerTile >= kMaxSkinnyN,
 constexpr int kRouteDot2 = 0;     // VALU dot2 kernel (q4_gemv.hip)
 constexpr int kRouteMfma = 1;     // 16x16x32 matrix-core kernel (q4_gemv_mfma.hip)
 constexpr int kRouteMfma4 = 2;    // 4x4x4 matrix-core kernel (q4_gemv_mfma4.hip)
-constexpr int kMfmaMinM = 7;      // smallest M routed to the 16x16x32 kernel
+constexpr int kMfmaMinM = 8;      // smallest M routed to the 16x16x32 kernel
 constexpr int kMfma4MinM = 4;     // M in [kMfma4MinM, kMfmaMinM) takes the 4x4x4 kernel
 constexpr int kMfma4SplitM = 3;   // at this M, rows longer than one 4x4x4 slice go there too
 constexpr int kMfma4SliceBlocks = 160;   // longest one-slice row of the 4x4x4 kernel (blocks)

@@ -139,16 +139,16 @@ def test_gemv_split_policy(L):
     assert slices(4, 4100, 5120) == 1         # 10 steps: one slice
     # ... and more slices only below 256 workgroups (16 rows each)
     assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
-    # the 4x4x4 kernel at M = 5 and 6 (two A operands): slices of at most 4
+    # the 4x4x4 kernel at M = 5..7 (two A operands): slices of at most 4
     # steps on 32-row tiles, from 5 steps on
-    for m in (5, 6):
+    for m in (5, 6, 7):
         assert slices(m, 5120, 17408) == 9, m
         assert slices(m, 5120, 5120) == 3, m   # 10 steps: 4 + 4 + 2
         assert slices(m, 4100, 2048) == 1, m   # 4 steps: one slice
     assert slices(5, 512, 5120) == 10          # 16 row tiles: one-step slices toward 256 workgroups
-    # 16x16x32 kernel (M >= 7): slices of at most 8 steps of 4 blocks, at
+    # 16x16x32 kernel (M >= 8): slices of at most 8 steps of 4 blocks, at
     # every width up to 16 (two activation staging items per thread past M = 8)
-    for m in (7, 8, 9, 13, 16):
+    for m in (8, 9, 13, 16):
         assert slices(m, 5120, 17408) == 17, m
     # ... and no more than that at or above 256 workgroups (64 rows each)
     assert slices(8, 5120, 5120) == 5          # 80 row tiles x 5 = 400 workgroups

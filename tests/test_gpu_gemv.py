@@ -45,10 +45,10 @@ def test_shapes_and_ragged_tails(m, n, k):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
-@pytest.mark.parametrize("m", [3, 4, 6])
+@pytest.mark.parametrize("m", [3, 4, 6, 7])
 def test_explicit_split_k(m, split):
     """The v_dot2 kernel (M = 3) and the 4x4x4 kernel with one (M = 4) and two
-    (M = 6) A operands with a forced slice count, over a ragged last row tile
+    (M = 6, 7) A operands with a forced slice count, over a ragged last row tile
     (N = 200)."""
     codes, scales, q, d = packed(200, 2048, 30)
     x = synthetic.activations(m, 2048, 31)
@@ -59,11 +59,11 @@ def test_explicit_split_k(m, split):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
 
-@pytest.mark.parametrize("m", [7, 13])
+@pytest.mark.parametrize("m", [8, 13])
 def test_explicit_split_k_matrix_core(m):
     """16x16x32 kernel with many slices (K = 4096, split_k = 64 gives 32
     one-step slices): the fixup's partial loads go out in several chunks
-    (18 slices per chunk at M = 7, 9 at M = 13), over a ragged last row tile."""
+    (18 slices per chunk at M = 8, 9 at M = 13), over a ragged last row tile."""
     codes, scales, q, d = packed(300, 4096, 40)
     x = synthetic.activations(m, 4096, 41 + m)
     ref = q4.matmul(x, q, d)
@@ -96,10 +96,10 @@ def test_workspace_shared_across_shapes():
         assert_close(host(yb), q4.matmul(xb, qb, db), what="shape B")
 
 
-@pytest.mark.parametrize("m", [4, 6, 8])
+@pytest.mark.parametrize("m", [4, 6, 7, 8])
 def test_one_hot_bit_exact(m):
     """x = e_k gives fp16(q[n,k] * d[n,k//32]): one product, rounded once
-    (M = 4, 6: the 4x4x4 kernel with one and two A operands; M = 8: the
+    (M = 4, 6, 7: the 4x4x4 kernel with one and two A operands; M = 8: the
     16x16x32 kernel)."""
     n, k = 96, 256
     codes, scales, q, d = packed(n, k, 40)
