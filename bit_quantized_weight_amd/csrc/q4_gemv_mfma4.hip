@@ -44,6 +44,9 @@ constexpr int kFixupBatch = 16;
 constexpr int kMaxSliceSteps = 10;         // the deepest copy of the kernel
 static_assert(kMaxSliceSteps * kStepBlocks == kMfma4SliceBlocks, "one-slice rows");
 constexpr int kSplitSliceSteps = 4;        // longest slice of a split row
+// Deepest copy with two row groups: with two A operands (M > 4) the 8- and
+// 10-step copies would spill registers.
+__host__ __device__ constexpr int max_pair_steps(int M) { return M > 4 ? 6 : kMaxSliceSteps; }
 constexpr int kWideTileMinWgs = 512;       // 64-row tiles only with this many workgroups
 constexpr int kMinWgs = 256;               // one workgroup per CU
 constexpr int kCachePolicyNT = 2;          // non-temporal: codes are read once, in whole lines
@@ -309,8 +312,10 @@ hipError_t launch_mr(const uint16_t* x, const uint8_t* codes, const uint16_t* sc
   const int steps = (p.blocks_per_split + kStepBlocks - 1) / kStepBlocks;
   if (steps <= 4) return launch_p<M, 4, R>(x, codes, scales, y, N, K, p, ws, s);
   if (steps <= 6) return launch_p<M, 6, R>(x, codes, scales, y, N, K, p, ws, s);
-  if (steps <= 8) return launch_p<M, 8, R>(x, codes, scales, y, N, K, p, ws, s);
-  if (steps <= kMaxSliceSteps) return launch_p<M, kMaxSliceSteps, R>(x, codes, scales, y, N, K, p, ws, s);
+  if constexpr (R == 1 || max_pair_steps(M) >= kMaxSliceSteps) {
+    if (steps <= 8) return launch_p<M, 8, R>(x, codes, scales, y, N, K, p, ws, s);
+    if (steps <= kMaxSliceSteps) return launch_p<M, kMaxSliceSteps, R>(x, codes, scales, y, N, K, p, ws, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -365,7 +370,8 @@ SkinnyPlan plan_skinny_mfma4(int M, int64_t N, int64_t K, int split_k) {
     while ((int64_t)S * p.row_tiles < kMinWgs && steps_total / (S + 1) >= 1) ++S;
   if (S < 1) S = 1;
   int sps = (steps_total + S - 1) / S;                 // steps per slice
-  if (sps > kMaxSliceSteps) sps = kMaxSliceSteps;
+  const int max_sps = groups == 2 ? max_pair_steps(M) : kMaxSliceSteps;
+  if (sps > max_sps) sps = max_sps;
   if (sps < 1) sps = 1;
   p.blocks_per_split = sps * kStepBlocks;
   p.splits = (nb + p.blocks_per_split - 1) / p.blocks_per_split;

@@ -137,6 +137,10 @@ def test_gemv_split_policy(L):
     assert slices(4, 5120, 17408) == 9        # 34 steps of 16 blocks: slices of 4
     assert slices(4, 4100, 11232) == 6        # 22 steps
     assert slices(4, 4100, 5120) == 1         # 10 steps: one slice
+    # forced slice counts are raised until a slice fits the deepest copy:
+    # 10 steps with one A operand, 6 with two (M = 5..7)
+    assert f(4, 1000, 17376, 2) == region + 4 * 4 * 1000 * 4
+    assert f(6, 1000, 17376, 2) == region + 6 * 6 * 1000 * 4
     # ... and more slices only below 256 workgroups (16 rows each)
     assert slices(1, 512, 8192) == 8          # 32 row tiles, 8 steps
     # the 4x4x4 kernel at M = 5..7 (two A operands): slices of at most 4

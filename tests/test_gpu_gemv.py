@@ -59,6 +59,20 @@ def test_explicit_split_k(m, split):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
 
+@pytest.mark.parametrize("m,split", [(4, 2), (6, 2), (7, 3)])
+def test_explicit_split_k_long_slices(m, split):
+    """A forced small slice count on a tall K (544 blocks, 34 steps): at M = 4
+    the slices are capped at 10 steps (4 slices), with two A operands at 6
+    steps (6 slices), over a ragged last row tile and a ragged last step."""
+    n, k = 1000, 17408 - 32
+    rows = tuple(np.unique(np.concatenate([[0, 31, 32, n - 1],
+                                           np.random.default_rng(m).integers(0, n, 40)])).tolist())
+    codes, scales, q, d = packed_sampled(n, k, 94, rows)
+    x = synthetic.activations(m, k, 95)
+    y = run(x, codes, scales, split)
+    assert_close(y[:, list(rows)], q4.matmul(x, q, d), what=f"M={m} split={split}")
+
+
 @pytest.mark.parametrize("m", [8, 13])
 def test_explicit_split_k_matrix_core(m):
     """16x16x32 kernel with many slices (K = 4096, split_k = 64 gives 32
