@@ -109,7 +109,15 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
 
 
-# Workspaces are cached per (device, size) so repeated calls do not allocate.
+def _need_shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# Workspaces are cached per (route, device, stream): calls on one stream run
+# in order, so they may share one; calls on two streams could overlap in time
+# and must not (their split-K counters, partials and quantized activations
+# would race).  A cached workspace only grows.
 _ws_cache = {}
 
 
@@ -117,7 +125,7 @@ def _workspace(nbytes, device, key):
     import torch
     if nbytes == 0:
         return None
-    k = (key, str(device))
+    k = (key, str(device), torch.cuda.current_stream(device).cuda_stream)
     buf = _ws_cache.get(k)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -141,15 +149,21 @@ def gemv_ws_bytes(m, n, k, split_k=0):
 
 
 def q4_gemv_skinny_raw(x, codes, scales, y, split_k=0, ws=None):
-    """Direct call into q4_gemv_skinny with caller-provided output (no allocation)."""
+    """Direct call into q4_gemv_skinny with a caller-provided output y [M, N]
+    and, optionally, workspace ws (uint8; its whole size is passed, so the
+    library rejects one that is too small)."""
+    import torch
     m, k = x.shape
     n = codes.shape[0]
-    nb = gemv_ws_bytes(m, n, k, split_k)
+    _need(y, torch.float16, "y")
+    _need_shape(y, (m, n), "y")
     if ws is None:
-        ws = _workspace(nb, x.device, "gemv")
+        ws = _workspace(gemv_ws_bytes(m, n, k, split_k), x.device, "gemv")
+    else:
+        _need(ws, torch.uint8, "ws")
     _check("q4_gemv_skinny", lib().q4_gemv_skinny(
         _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, split_k,
-        _ptr(ws), nb, _stream()))
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
     return y
 
 
@@ -186,6 +200,8 @@ def a8w4_gemm(x, codes, scales, y=None):
     n = codes.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _need(y, torch.float16, "y")
+    _need_shape(y, (m, n), "y")
     nb = a8w4_ws_bytes(m, k)
     ws = _workspace(nb, x.device, "a8")
     _check("a8w4_gemm_prefill", lib().a8w4_gemm_prefill(
@@ -211,6 +227,9 @@ def a8w4_gemm_prepared(ws, m, k, codes, scales, y=None):
     n = codes.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=torch.float16, device=codes.device)
+    _need(y, torch.float16, "y")
+    _need_shape(y, (m, n), "y")
+    _need(ws, torch.uint8, "ws")
     _check("a8w4_gemm_prepared", lib().a8w4_gemm_prepared(
         _ptr(ws), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, ws.numel(), _stream()))
     return y

@@ -329,8 +329,18 @@ hipError_t launch_m(const uint16_t* x, const uint8_t* codes, const uint16_t* sca
     }
     return hipErrorInvalidValue;
   }
-  if (p.rows_per_wg == 8 * kWaves) return launch_mr<M, 2>(x, codes, scales, y, N, K, p, ws, s);
-  return launch_mr<M, 1>(x, codes, scales, y, N, K, p, ws, s);
+  if constexpr (M == 3) {
+    // M = 3 comes here only for rows split by the default plan (a forced
+    // split_k keeps M = 3 on the v_dot2 kernel): slices of at most 4 steps on
+    // two or four row groups, so no other copy is built.
+    if (p.rows_per_wg == 8 * kWaves &&
+        (p.blocks_per_split + kStepBlocks - 1) / kStepBlocks <= kSplitSliceSteps)
+      return launch_p<M, kSplitSliceSteps, 2>(x, codes, scales, y, N, K, p, ws, s);
+    return hipErrorInvalidValue;
+  } else {
+    if (p.rows_per_wg == 8 * kWaves) return launch_mr<M, 2>(x, codes, scales, y, N, K, p, ws, s);
+    return launch_mr<M, 1>(x, codes, scales, y, N, K, p, ws, s);
+  }
 }
 
 }  // namespace

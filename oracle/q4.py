@@ -125,10 +125,3 @@ def matmul_blockwise(x, q, d):
         sl = slice(b * BLOCK, (b + 1) * BLOCK)
         y += (x64[:, sl] @ q64[:, sl].T) * d64[:, b][None, :]
     return y
-
-
-def matmul_rows(x, w_rows):
-    """Oracle for a subset of output rows: quantize the given fp32 rows of W and
-    return (Y[:, rows] float64, codes, d) -- used to spot-check large shapes."""
-    q, d = quantize(w_rows)
-    return matmul(x, q, d), q, d

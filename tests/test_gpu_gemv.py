@@ -59,6 +59,21 @@ def test_explicit_split_k(m, split):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16)), "split-K not deterministic"
 
 
+@pytest.mark.parametrize("m", [5, 7])
+@pytest.mark.parametrize("k", [2080, 5120, 8192])
+def test_forced_one_slice_two_operands(m, k):
+    """split_k = 1 with two A operands (M = 5, 7) on the 4x4x4 kernel: one
+    slice of 5 steps (the 6-step copy), of 10 steps (the 10-step copy, the
+    largest LDS use: 76.8 KB at M = 7), and K = 8192 capped at 10 steps (two
+    slices).  Ragged last row tile (N = 200)."""
+    codes, scales, q, d = packed(200, k, 96)
+    x = synthetic.activations(m, k, 97 + m)
+    ref = q4.matmul(x, q, d)
+    y1 = run(x, codes, scales, 1)
+    assert_close(y1, ref, what=f"M={m} K={k} split_k=1")
+    assert np.array_equal(run(x, codes, scales, 1).view(np.uint16), y1.view(np.uint16))
+
+
 @pytest.mark.parametrize("m,split", [(4, 2), (6, 2), (7, 3)])
 def test_explicit_split_k_long_slices(m, split):
     """A forced small slice count on a tall K (544 blocks, 34 steps): at M = 4
@@ -182,7 +197,7 @@ def test_invariants_bit_exact():
     only: the hardware fp16 dot product does not round symmetrically in sign,
     so negation can move a result by one fp16 ulp."""
     codes, scales, q, d = packed(5120, 17408, synthetic.WEIGHT_SEED)
-    for m in (2, 4, 6, 8):    # v_dot2, 4x4x4 (one and two A operands), 16x16x32
+    for m in (1, 2, 3, 4, 5, 6, 8):   # v_dot2, 4x4x4 (one and two A operands), 16x16x32
         x = synthetic.activations(m, 17408, 50)
         y = run(x, codes, scales)
         y2 = run((x.astype(np.float32) * 2).astype(np.float16), codes, scales)
@@ -191,10 +206,10 @@ def test_invariants_bit_exact():
         assert np.array_equal(y2[normal], twice[normal]), m
         gap = np.abs(y2[~normal].astype(np.float64) - twice[~normal].astype(np.float64))
         assert np.all(gap <= 1.5 * 2.0 ** -24), (m, gap.max())
-    yn = run(-x, codes, scales)
-    assert_close(-yn, q4.matmul(x, q, d), what="negated input")
-    for _ in range(10):
-        assert np.array_equal(run(x, codes, scales).view(np.uint16), y.view(np.uint16))
+        yn = run(-x, codes, scales)
+        assert_close(-yn, q4.matmul(x, q, d), what=f"negated input M={m}")
+        for _ in range(5):
+            assert np.array_equal(run(x, codes, scales).view(np.uint16), y.view(np.uint16)), m
 
 
 def test_permuted_rows_permute_outputs():
@@ -384,3 +399,52 @@ def test_one_hot_bit_exact_wide():
             kk = start + r
             want = (q[:, kk].astype(np.float64) * d[:, kk // 32].astype(np.float64)).astype(np.float16)
             assert np.array_equal(y[r], want), kk
+
+
+def test_binding_rejects_short_workspace_and_bad_output():
+    """The binding passes the caller's whole workspace size, so a workspace
+    one byte short of what the plan needs is rejected by the library
+    (WORKSPACE) before anything is enqueued; a y of the wrong shape or dtype
+    is rejected by the binding."""
+    torch = torch_cuda()
+    from bit_quantized_weight_amd import Q4WError, gemv_ws_bytes, q4_gemv_skinny_raw
+    codes, scales, q, d = packed(200, 2048, 30)
+    x = dev(synthetic.activations(4, 2048, 31), torch)
+    need = gemv_ws_bytes(4, 200, 2048, 3)
+    assert need > 0
+    short = torch.zeros(need - 1, dtype=torch.uint8, device="cuda")
+    y = torch.empty((4, 200), dtype=torch.float16, device="cuda")
+    with pytest.raises(Q4WError) as e:
+        q4_gemv_skinny_raw(x, codes, scales, y, split_k=3, ws=short)
+    assert e.value.status == -4
+    with pytest.raises(ValueError):
+        q4_gemv_skinny_raw(x, codes, scales, torch.empty((4, 199), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        q4_gemv_skinny_raw(x, codes, scales, torch.empty((4, 200), dtype=torch.float32, device="cuda"))
+    ok = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    q4_gemv_skinny_raw(x, codes, scales, y, split_k=3, ws=ok)
+    torch.cuda.synchronize()
+    assert_close(host(y), q4.matmul(synthetic.activations(4, 2048, 31), q, d), what="exact workspace")
+
+
+def test_workspace_cache_is_per_stream():
+    """Calls on two streams get two cached workspaces (their split-K state
+    must not be shared), calls on one stream share one."""
+    torch = torch_cuda()
+    from bit_quantized_weight_amd import binding
+    codes, scales, q, d = packed(200, 2048, 30)
+    xh = synthetic.activations(4, 2048, 31)
+    x = dev(xh, torch)
+    ref = q4.matmul(xh, q, d)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ys = []
+    for s in (s1, s2, s1):
+        with torch.cuda.stream(s):
+            ys.append(gemv(x, codes, scales, split_k=3))
+    torch.cuda.synchronize()
+    keys = [k for k in binding._ws_cache if k[0] == "gemv"]
+    streams = {k[2] for k in keys}
+    assert s1.cuda_stream in streams and s2.cuda_stream in streams
+    for y in ys:
+        assert_close(host(y), ref, what="per-stream workspace")
