@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     batched_plan,
     batched_ws_bytes,
     gemv,
+    gemv_noalloc,
     gemv_ws_bytes,
     lib,
     lib_path,

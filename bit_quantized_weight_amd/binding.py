@@ -63,6 +63,8 @@ def lib():
     L.q4_gemv_skinny_ws_bytes.restype = sz
     L.q4_gemv_skinny.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp, sz, vp]
     L.q4_gemv_skinny.restype = i32
+    L.q4_gemv_skinny_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp]
+    L.q4_gemv_skinny_noalloc.restype = i32
     L.a8_quantize_act.argtypes = [vp, i64, i64, vp, vp, vp]
     L.a8_quantize_act.restype = i32
     L.a8w4_ws_bytes.argtypes = [i64, i64]
@@ -175,6 +177,28 @@ def gemv(x, codes, scales, split_k=0):
     _need(scales, torch.float16, "scales")
     y = torch.empty((x.shape[0], codes.shape[0]), dtype=torch.float16, device=x.device)
     return q4_gemv_skinny_raw(x, codes, scales, y, split_k)
+
+
+# Q4W_NOALLOC_SCRATCH_BYTES of include/q4w.h: the largest split-K workspace
+# q4_gemv_skinny_noalloc serves from its static device scratch.
+NOALLOC_SCRATCH_BYTES = 256 * 1024 + 8 * 1024 * 1024
+
+
+def gemv_noalloc(x, codes, scales, y, split_k=0):
+    """q4_gemv_skinny_noalloc into a caller-provided fp16 y [M, N]: no
+    workspace argument, nothing allocated (the library's static device
+    scratch holds the split-K state)."""
+    import torch
+    _need(x, torch.float16, "x")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float16, "scales")
+    m, k = x.shape
+    n = codes.shape[0]
+    _need(y, torch.float16, "y")
+    _need_shape(y, (m, n), "y")
+    _check("q4_gemv_skinny_noalloc", lib().q4_gemv_skinny_noalloc(
+        _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, split_k, _stream()))
+    return y
 
 
 def a8_quantize_act(x):

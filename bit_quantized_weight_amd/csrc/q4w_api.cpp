@@ -6,6 +6,7 @@
 #include "q4w_internal.h"
 
 #include <climits>
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -50,6 +51,67 @@ q4w::BatchedLayout batch_layout(int M, const q4w_gemv_desc* d, int count,
   return q4w::batched_layout(M, count, N.data(), K.data());
 }
 
+// Checks of the skinny entry points, all before any HIP call.  Returns a
+// negative status, 1 when there is nothing to do (N == 0), 2 when y is to be
+// zero-filled (K == 0), or 0 with *plan filled for a launch.
+int skinny_checks(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, const uint16_t* y,
+                  int M, int64_t N, int64_t K, int split_k, q4w::SkinnyPlan* plan) {
+  if (N < 0 || K < 0 || split_k < 0 || split_k > 64) return Q4W_ERR_INVALID_ARG;
+  if (M < 1 || M > q4w::kMaxSkinnyM || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N > q4w::kMaxSkinnyN || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (N == 0) return 1;
+  if (!y) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(y, 4)) return Q4W_ERR_MISALIGNED;
+  if (K == 0) return 2;
+  if (!x || !codes || !scales) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return Q4W_ERR_MISALIGNED;
+  *plan = q4w::plan_skinny(M, N, K, split_k);
+  return Q4W_OK;
+}
+
+}  // namespace
+
+// ---- scratch of the allocation-free skinny entry point ----------------------
+// The split-K workspace of q4_gemv_skinny_noalloc (arrival counters, then fp32
+// partials) is this file-scope device array; every device holds its own copy
+// until the process ends.  In host code the name `scratch` stands for a
+// host-side shadow, never for device memory: the device address is obtained
+// with hipGetSymbolAddress, once per device, and only that address is passed
+// to kernels.
+static_assert(Q4W_NOALLOC_SCRATCH_BYTES > q4w::kCounterRegionBytes, "room for partials");
+static_assert(Q4W_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte lines");
+static __device__ __align__(256) unsigned char scratch[Q4W_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device.  The first call on a
+// device looks the address up and enqueues, on `stream`, a fill kernel that
+// zeroes the counter region (every completed skinny call leaves it zeroed
+// again, so this is needed once).
+hipError_t scratch_on_current_device(void** out, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || !aligned(p, 256)) return hipErrorInvalidSymbol;
+    e = q4w::launch_fill_zero_u16(static_cast<uint16_t*>(p),
+                                  (int64_t)(q4w::kCounterRegionBytes / sizeof(uint16_t)), stream);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,19 +136,31 @@ size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k) {
 int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
                    int M, int64_t N, int64_t K, int split_k, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
-  if (N < 0 || K < 0 || split_k < 0 || split_k > 64) return Q4W_ERR_INVALID_ARG;
-  if (M < 1 || M > q4w::kMaxSkinnyM || K % q4w::kBlock != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (N > q4w::kMaxSkinnyN || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (N == 0) return Q4W_OK;
-  if (!y) return Q4W_ERR_INVALID_ARG;
-  if (!aligned(y, 4)) return Q4W_ERR_MISALIGNED;
-  if (K == 0) return hip_status(q4w::launch_fill_zero_u16(y, int64_t(M) * N, stream));
-  if (!x || !codes || !scales) return Q4W_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return Q4W_ERR_MISALIGNED;
-  const q4w::SkinnyPlan p = q4w::plan_skinny(M, N, K, split_k);
+  q4w::SkinnyPlan p{};
+  const int c = skinny_checks(x, codes, scales, y, M, N, K, split_k, &p);
+  if (c < 0) return c;
+  if (c == 1) return Q4W_OK;
+  if (c == 2) return hip_status(q4w::launch_fill_zero_u16(y, int64_t(M) * N, stream));
   if (p.ws_bytes > 0) {
     if (!ws || ws_bytes < p.ws_bytes) return Q4W_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  }
+  return hip_status(q4w::launch_skinny(x, codes, scales, y, M, N, K, p, ws, stream));
+}
+
+int q4_gemv_skinny_noalloc(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                           uint16_t* y, int M, int64_t N, int64_t K, int split_k,
+                           hipStream_t stream) {
+  q4w::SkinnyPlan p{};
+  const int c = skinny_checks(x, codes, scales, y, M, N, K, split_k, &p);
+  if (c < 0) return c;
+  if (c == 1) return Q4W_OK;
+  if (c == 2) return hip_status(q4w::launch_fill_zero_u16(y, int64_t(M) * N, stream));
+  if (p.ws_bytes > Q4W_NOALLOC_SCRATCH_BYTES) return Q4W_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    const hipError_t e = scratch_on_current_device(&ws, stream);
+    if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(q4w::launch_skinny(x, codes, scales, y, M, N, K, p, ws, stream));
 }

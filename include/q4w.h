@@ -30,7 +30,9 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers (hipMalloc'd or equivalent),
  *     owned by the caller; the library never allocates or frees memory and
- *     keeps no state besides a per-thread copy of the last HIP error.
+ *     keeps no state besides a per-thread copy of the last HIP error and the
+ *     static device scratch of q4_gemv_skinny_noalloc (with its address per
+ *     device).
  *   - Half-precision values cross the ABI as uint16_t bit patterns.
  *   - `stream` is the caller's HIP stream (NULL = default stream).  Each call
  *     only enqueues work and returns; results are valid once the stream is
@@ -94,6 +96,35 @@ size_t q4_gemv_skinny_ws_bytes(int M, int64_t N, int64_t K, int split_k);
 int q4_gemv_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
                    uint16_t* y, int M, int64_t N, int64_t K, int split_k,
                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * q4_gemv_skinny_noalloc: for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc) and so cannot provide the workspace of q4_gemv_skinny.  Same
+ *   arguments, checks and result as q4_gemv_skinny without ws / ws_bytes: the
+ *   same plan and kernels run, so the output is bit-identical to
+ *   q4_gemv_skinny's for the same inputs.  The split-K workspace is instead a
+ *   static device array of Q4W_NOALLOC_SCRATCH_BYTES bytes inside the
+ *   library (a 256 KiB counter region, then 8 MiB of fp32 partials: the
+ *   default plan of every M <= 16 fits for the projections (K, N) = (5120,
+ *   7168), (5120, 5120), (5120, 17408) and (17408, 5120)), which each device
+ *   the library runs on holds until the process ends.  Nothing is allocated
+ *   or freed.
+ *   A plan that needs more than Q4W_NOALLOC_SCRATCH_BYTES (see
+ *   q4_gemv_skinny_ws_bytes) returns Q4W_ERR_WORKSPACE before anything is
+ *   enqueued.
+ *   The first call on a device (with that device current; not under graph
+ *   capture) looks up the array's device address and enqueues on `stream`
+ *   one small kernel that zeroes its counter region; every completed call
+ *   leaves the counters zeroed again and overwrites every partial before
+ *   reading it.  All calls on one device share the array: calls that overlap
+ *   in time on one device (two streams, two threads) race and give wrong
+ *   results.
+ */
+#define Q4W_NOALLOC_SCRATCH_BYTES (256u * 1024u + 8u * 1024u * 1024u)
+int q4_gemv_skinny_noalloc(const uint16_t* x, const uint8_t* codes, const uint16_t* scales,
+                           uint16_t* y, int M, int64_t N, int64_t K, int split_k,
+                           hipStream_t stream);
 
 /*
  * a8_quantize_act: per token m and 64-channel group g,

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
               "a8w4_gemm_prefill", "a8w4_ws_bytes", "a8w4_debug_block_acc",
               "a8w4_prepare_act", "a8w4_gemm_prepared",
               "q4_gemv_batched_ws_bytes", "q4_gemv_batched_plan", "q4_gemv_batched_run",
+              "q4_gemv_skinny_noalloc",
               "q4w_status_str", "q4w_last_hip_error"]:
         assert n in names, n
 
@@ -92,6 +93,35 @@ def test_gemv_checks(L):
     assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, NUL, 0, NUL) == WS
     assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, p(A), ws - 1, NUL) == WS
     assert g(p(A), p(A), p(A), p(A), 4, 5120, 17408, 0, p(A + 16), ws, NUL) == ALIGN
+
+
+def test_gemv_noalloc_checks(L):
+    """The allocation-free entry point makes the same checks as q4_gemv_skinny
+    and rejects a plan larger than its static scratch, all before any HIP
+    call."""
+    g = L.q4_gemv_skinny_noalloc
+    assert g(p(A), p(A), p(A), p(A), 0, 64, 64, 0, NUL) == SHAPE
+    assert g(p(A), p(A), p(A), p(A), 17, 64, 64, 0, NUL) == SHAPE
+    assert g(p(A), p(A), p(A), p(A), 1, 64, 48, 0, NUL) == SHAPE
+    assert g(p(A), p(A), p(A), p(A), 1, 64, 64, 65, NUL) == INVALID
+    assert g(p(A), p(A), p(A), p(A), 1, 0, 64, 0, NUL) == OK          # N == 0: no-op
+    assert g(p(A), p(A), p(A), NUL, 1, 64, 64, 0, NUL) == INVALID
+    assert g(p(U), p(A), p(A), p(A), 1, 64, 64, 0, NUL) == ALIGN
+    assert g(p(A), p(A), p(A), p(A + 2), 1, 64, 64, 0, NUL) == ALIGN
+    # the gate and up projections as one (N = 34816) at M = 16 need more
+    # split-K scratch than the static array holds
+    big = L.q4_gemv_skinny_ws_bytes(16, 34816, 5120, 0)
+    assert big > binding.NOALLOC_SCRATCH_BYTES
+    assert g(p(A), p(A), p(A), p(A), 16, 34816, 5120, 0, NUL) == WS
+    for m in range(1, 17):
+        for k, n in ((5120, 7168), (5120, 5120), (5120, 17408), (17408, 5120)):
+            assert L.q4_gemv_skinny_ws_bytes(m, n, k, 0) <= binding.NOALLOC_SCRATCH_BYTES, (m, k, n)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define Q4W_NOALLOC_SCRATCH_BYTES \((.*)\)", text)
+    assert m and eval(m.group(1).replace("u", "")) == binding.NOALLOC_SCRATCH_BYTES
 
 
 def test_gemv_ws_sizes(L):
