@@ -21,10 +21,11 @@
 //    0x4B400000 (1.5 * 2^23), so the int32 result read as fp32 is exactly
 //    12582912 + 16 I; two FMAs per group fold both block scales and remove
 //    the offset, one FMA applies the activation scale.
-//  * Activations are quantized into the workspace in the MFMA operand order
-//    (one 1 KB coalesced load per 32x32 operand); weight codes and scales are
-//    staged through LDS with an XOR swizzle (conflict-free 128-bit reads) and
-//    halves are exchanged across the wave with v_permlane32_swap.
+//  * Activations are quantized into the workspace in the MFMA operand order,
+//    so a wave copies each 32 x 32 operand (1 KB) from the workspace straight
+//    into LDS with one buffer load that writes LDS; weight codes are unpacked
+//    into LDS with an XOR swizzle (conflict-free 128-bit reads), and each
+//    column's two block scales and the magic offset sit in one 16-byte entry.
 
 #include "q4w_internal.h"
 #include <hip/hip_fp16.h>
@@ -163,10 +164,14 @@ __global__ void __launch_bounds__(64) act_quant_tiled_kernel(const uint16_t* __r
 // ---- int8 MFMA GEMM --------------------------------------------------------
 // The fp32 rescale (1.5 FMAs per output element and 32-wide block, the
 // three-FMA magic-number form) costs three times the MFMA issue time, so the
-// kernel is VALU-bound and keeps every other VALU op out of the inner loop:
-// the nibble -> int8 unpack and the weight-scale preparation are done once
-// per workgroup into LDS.  Every operand a wave needs is staged in LDS one
-// chunk ahead (double buffer), so a wave only waits on LDS, and two
+// kernel is VALU-bound.  Everything else is kept off the VALU where it can
+// be: the nibble -> int8 unpack and the weight-scale preparation are done
+// once per workgroup into LDS, the activation tile is copied from the
+// workspace straight into LDS by buffer loads with the LDS destination (no
+// registers, no VALU), and the matrix-core products are software-pipelined
+// one 32 x 32 subtile ahead of their rescale, so a wave issues the next
+// pair of MFMAs and then rescales the previous pair while they run.  Every
+// operand is staged in LDS one chunk ahead (double buffer), and two
 // workgroups fit on a CU.
 constexpr int kTM = 128;          // workgroup tile rows (tokens)
 constexpr int kTN = 128;          // workgroup tile columns (output features)
@@ -175,29 +180,32 @@ constexpr int kChunkGroups = kChunkBlocks / 2;
 constexpr int kMSub = kTM / 32;   // 32-row MFMA subtiles per workgroup
 constexpr int kNSub = kTN / 32;   // 32-column MFMA subtiles per workgroup
 constexpr float kMagic = 12582912.0f;   // 0x4B400000 = 1.5 * 2^23
-constexpr int kSdStride = kTN + 16;       // padding spreads the staging writes over all banks
 constexpr int kA8NarrowTiles = 256;      // fewer 128-row tiles than CUs: use 64-row tiles
 
 __device__ __forceinline__ uint32_t lo_codes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_codes(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-// One LDS chunk buffer (36 KB).
+// One LDS chunk buffer (35 KB).
 //   bq: int8 B operands (16 x the codes), [n-subtile][block][slot], 16 B per
 //       slot; the operand of MFMA lane l for block b sits in slot l ^ 4b, so
 //       the staging writes (4 rows x 4 blocks per 16 lanes) and the operand
 //       reads (16 consecutive lanes) both touch 16 distinct bank groups.
-//   aq: int8 A operands, [m-subtile][block][lane] (copied from the tiled
-//       activation layout).
-//   sd: d[n, b] / 16 (fp32), [block][column + pad].
-//   sb: -1.5 * 2^23 * (d[n, 2g] + d[n, 2g+1]) / 16, [group][column].
+//   aq: int8 A operands, [m-subtile][block][lane], a straight copy of the
+//       tiled activation layout.
+//   dn: per group and column, {d[n, 2g] / 16, d[n, 2g+1] / 16}: one 8-byte
+//       read gives a lane both block scales of its column.
 //   sa: activation scales, [group][row].
 struct ChunkLds {
   uint4 bq[kNSub * kChunkBlocks * 64];
   uint4 aq[kMSub * kChunkBlocks * 64];
-  float sd[kChunkBlocks * kSdStride];
-  float sb[kChunkGroups * kTN];
+  float2 dn[kChunkGroups * kTN];
   float sa[kChunkGroups * kTM];
 };
+// The raw codes of one chunk (128 rows x 4 blocks, 8 KB), copied from memory
+// straight into LDS; unpacked into a chunk buffer's bq at the chunk's commit.
+constexpr int kRawUnits = kTN * kChunkBlocks;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // kMS: 32-row M subtiles per workgroup, 4 (128 x 128 tiles) or 2 (64 x 128
 // tiles, twice the workgroups for short prompts); each wave takes kMS / 2.
@@ -207,7 +215,8 @@ struct ChunkLds {
 // workgroup.  A tile cut by a range boundary is summed by the workgroups
 // that share it: each writes its fp32 partial tile to the workspace, and the
 // last to arrive adds the parts in range order (a fixed order: the result
-// does not depend on which arrives last) and stores y.
+// does not depend on which arrives last) and stores y.  With kDebug every
+// chunk's block sums are written by the one workgroup that computes them.
 template <bool kDebug, int kMS, bool kSplit>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -216,21 +225,27 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
                  uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg, int M, int N, int K,
                  int mtiles, int ntiles, int upw, float* __restrict__ partial,
                  uint32_t* __restrict__ counters) {
-  __shared__ ChunkLds lds[2];
+  // The two chunk buffers are separate objects (not one array) so that the
+  // compiler can tell the buffer being read from the one the next chunk's
+  // loads are writing into; with one array it waits for those loads before
+  // every LDS read.
+  __shared__ ChunkLds lds0, lds1;
+  __shared__ uint4 rawq[kRawUnits];
   __shared__ int is_last;
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   static_assert(kMS == 2 || kMS == 4, "64- or 128-row tiles");
-  static_assert(!(kSplit && kDebug), "the debug epilogue runs whole tiles");
   constexpr int TM = 32 * kMS;      // rows (tokens) of this workgroup's tile
   constexpr int kMI = kMS / 2;      // 32-row subtiles per wave
+  constexpr int kUPG = 2 * kMI;     // 32 x 32 subtiles (units) of a wave per group
+  constexpr int kUnits = kChunkGroups * kUPG;
 
   const int nb = K / kBlock;
   const int G = K / kActGroup;
   const int nchunks = (nb + kChunkBlocks - 1) / kChunkBlocks;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int lane = tid & 63;
-  const int wm = wave >> 1;          // 2 x 2 waves, each 64 x 64
+  const int wm = wave >> 1;          // 2 x 2 waves, each (32 kMI) x 64
   const int wn = wave & 1;
   const int j = lane & 31;
   const int h = lane >> 5;
@@ -240,15 +255,14 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   for (int v = 0; v < 16; ++v) magic[v] = 0x4B400000;
   float acc[kMI][2][16];
 
-  // Per-lane LDS byte offsets inside a chunk buffer; every operand read of
-  // the unrolled group loop below is one of these plus a compile-time offset.
+  // Per-lane LDS byte offsets inside a chunk buffer; every operand read below
+  // is one of these plus a compile-time offset.
   const int off_a = (int)offsetof(ChunkLds, aq) + ((wm * kMI * kChunkBlocks) * 64 + lane) * 16;
   int off_b[kChunkBlocks];
 #pragma unroll
   for (int bl = 0; bl < kChunkBlocks; ++bl)
     off_b[bl] = (int)offsetof(ChunkLds, bq) + ((wn * 2 * kChunkBlocks) * 64 + (lane ^ (4 * bl))) * 16;
-  const int off_sd = (int)offsetof(ChunkLds, sd) + (wn * 64 + j) * 4;
-  const int off_sb = (int)offsetof(ChunkLds, sb) + (wn * 64 + j) * 4;
+  const int off_dn = (int)offsetof(ChunkLds, dn) + (wn * 64 + j) * 8;
   const int off_sa = (int)offsetof(ChunkLds, sa) + (wm * 32 * kMI + 4 * h) * 4;
 
   // ---- chunks [c0, c1) of tile t into acc ---------------------------------
@@ -271,80 +285,77 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
     const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(scales + (size_t)n_base * nb), 0, rows_here * nb * 2, 0x00020000);
 
-    // ---- cooperative chunk staging --------------------------------------------
-    // per thread: 2 weight units (row, block), kMS activation units, 2 scales, 1 sa
-    uint4 rawb[2], rawa[kMS];
-    uint32_t rawd[2];
+    // ---- cooperative chunk staging ------------------------------------------
+    // The weight codes (2 units (row, block) of 16 B per thread) and the
+    // activation tile (kMS units per thread) go straight to LDS; unless
+    // kDebug, one pair of block scales (row, group) and one activation scale
+    // per thread go through registers.  The
+    // per-lane offsets are fixed for the segment; a chunk adds uniform steps.
+    // In a chunk past the last block (K % 128 == 64) the code loads of blocks
+    // nb, nb + 1 read the next row's first blocks (the buffer range check
+    // gives zeros past the last row) and the activation loads the next
+    // subtile's: finite values whose group is multiplied by d = 0, because
+    // the scale loads, like the activation-scale loads, are masked to zero
+    // past the last block.
+    uint32_t rawd;
     float rawsa;
-    auto stage_issue = [&](int c) {
+    const uint32_t ob = (uint32_t)(((tid >> 2) * nb + (tid & 3)) * kBlockBytes);   // unit it: + it * 64 rows
+    const uint32_t ob_rows = (uint32_t)(64 * nb * kBlockBytes);
+    const uint32_t oa = (uint32_t)((wave * 64 + lane) * 16);
+    const int sgi = tid >> 7;                                  // scale pair: group of the chunk
+    const uint32_t od = (uint32_t)(((tid & 127) * nb + 2 * sgi) * 2);
+    const int agi = tid / TM;                                  // activation scale: group of the chunk
+    const uint32_t osa = (uint32_t)((((tid % TM) >> 5) * G * 32 + (tid & 31)) * 4);
+    auto stage_issue = [&](int c, ChunkLds& L) {
   #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int u = it * 256 + tid;          // 128 rows x 4 blocks
-        const int r = u >> 2, bl = u & 3;
-        const int b = c * kChunkBlocks + bl;
-        const uint32_t off = (b < nb) ? (uint32_t)((r * nb + b) * kBlockBytes) : 0x80000000u;
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
-        rawb[it] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
+      for (int it = 0; it < 2; ++it)    // unit it * 256 + tid of rawq: row tid / 4 + 64 it, block tid % 4
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rc, (lds_ptr_t)(&rawq[it * 256 + wave * 64]), 16, ob + it * ob_rows + c * kChunkBlocks * kBlockBytes,
+            0, 0, 0);
+      // activation operands: wave w copies, for every m-subtile it, the
+      // 1 KB of block c * 4 + w (64 lanes x 16 B) to aq[it][w][lane]
   #pragma unroll
-      for (int it = 0; it < kMS; ++it) {
-        const int u = it * 256 + tid;          // kMS m-subtiles x 4 blocks x 64 lanes
-        const int ms = u >> 8, bl = (u >> 6) & 3, l = u & 63;
-        const int b = c * kChunkBlocks + bl;
-        const uint32_t off = (b < nb) ? (uint32_t)(((ms * nb + b) * 64 + l) * 16) : 0x80000000u;
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-        rawa[it] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
+      for (int it = 0; it < kMS; ++it)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (lds_ptr_t)(&L.aq[(it * kChunkBlocks + wave) * 64]), 16, oa,
+            (it * nb + c * kChunkBlocks) * 64 * 16, 0, 0);
       if (!kDebug) {
-  #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const int u = it * 256 + tid;        // 128 columns x 4 blocks
-          const int r = u >> 2, bl = u & 3;
-          const int b = c * kChunkBlocks + bl;
-          const uint32_t off = (b < nb) ? (uint32_t)((r * nb + b) * 2) : 0x80000000u;
-          rawd[it] = __builtin_amdgcn_raw_buffer_load_b16(rsc, off, 0, 0);
-        }
-        {
-          const int gi = tid / TM, r = tid % TM;  // 2 groups x TM rows
-          const int g = c * kChunkGroups + gi;
-          const int ms = r >> 5, rr = r & 31;
-          const uint32_t off = (gi < kChunkGroups && g < G) ? (uint32_t)(((ms * G + g) * 32 + rr) * 4)
-                                                            : 0x80000000u;
-          rawsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, off, 0, 0));
-        }
+        const bool dlive = c * kChunkBlocks + 2 * sgi < nb;
+        rawd = __builtin_amdgcn_raw_buffer_load_b32(rsc, dlive ? od + c * kChunkBlocks * 2 : 0x80000000u, 0, 0);
+        const int g = c * kChunkGroups + agi;
+        const bool alive = agi < kChunkGroups && g < G;
+        rawsa = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rsa, alive ? osa + g * 32 * 4 : 0x80000000u, 0, 0));
       }
     };
+    // Waits for the chunk's loads (the raw codes a thread unpacks are the
+    // ones its own lane copied into LDS).
     auto stage_commit = [&](ChunkLds& L) {
+      __builtin_amdgcn_s_waitcnt(0);
+      // keep the scale conversions here, not next to the loads (they would
+      // wait for them at the start of the chunk)
+      if (!kDebug) asm volatile("" : "+v"(rawd), "+v"(rawsa));
   #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int u = it * 256 + tid;
         const int r = u >> 2, bl = u & 3;
         const int ns = r >> 5, jj = r & 31;
-        const uint4 w = rawb[it];
+        const uint4 w = rawq[u];
         // K-half 0 of the block is code words 0-1, half 1 is words 2-3
         L.bq[(ns * kChunkBlocks + bl) * 64 + (jj ^ (4 * bl))] =
             make_uint4(lo_codes(w.x), hi_codes(w.x), lo_codes(w.y), hi_codes(w.y));
         L.bq[(ns * kChunkBlocks + bl) * 64 + ((jj + 32) ^ (4 * bl))] =
             make_uint4(lo_codes(w.z), hi_codes(w.z), lo_codes(w.w), hi_codes(w.w));
       }
-  #pragma unroll
-      for (int it = 0; it < kMS; ++it) L.aq[it * 256 + tid] = rawa[it];
       if (!kDebug) {
-  #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const int u = it * 256 + tid;
-          const int r = u >> 2, bl = u & 3;
-          // the B operand carries 16 q: fold the 1/16 into the scale (exact)
-          const float d = __half2float(__ushort_as_half((unsigned short)rawd[it])) * 0.0625f;
-          L.sd[bl * kSdStride + r] = d;
-          // blocks 2i and 2i+1 of a group sit in adjacent lanes
-          const float dn = __shfl_xor(d, 1, 64);
-          if ((bl & 1) == 0) L.sb[(bl >> 1) * kTN + r] = -kMagic * (d + dn);
-        }
+        // the B operand carries 16 q: fold the 1/16 into the scales (exact).
+        // Past the last block the loads read zeros: d = 0, so the group adds 0.
+        const float d0 = __half2float(__ushort_as_half((unsigned short)(rawd & 0xFFFFu))) * 0.0625f;
+        const float d1 = __half2float(__ushort_as_half((unsigned short)(rawd >> 16))) * 0.0625f;
+        L.dn[tid] = make_float2(d0, d1);
         if (tid < kChunkGroups * TM) L.sa[tid] = rawsa;
       }
     };
-
 
 #pragma unroll
     for (int a = 0; a < kMI; ++a)
@@ -353,82 +364,138 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    stage_issue(c0);
-    stage_commit(lds[0]);
+    stage_issue(c0, lds0);
+    stage_commit(lds0);
+    __builtin_amdgcn_s_waitcnt(0);      // the activation tile has landed in LDS
     __syncthreads();
 
-#pragma unroll 1
-    for (int c = c0; c < c1; ++c) {
-      const char* L = reinterpret_cast<const char*>(&lds[(c - c0) & 1]);
-      stage_issue(c + 1 < c1 ? c + 1 : nchunks);   // past the segment: out of range
+    // chunk c: computed from cur while chunk c + 1 is loaded into nxt
+    auto chunk = [&](int c, const ChunkLds& cur, ChunkLds& nxt) {
+      const char* L = reinterpret_cast<const char*>(&cur);
+      if (c + 1 < c1) stage_issue(c + 1, nxt);
+
+      // Unit u = (group gi, m-subtile mi, n-subtile ni) is one 32 x 32
+      // subtile of one group: two MFMAs (the group's two blocks), then 16
+      // values x 3 FMAs of rescale.  The MFMAs of unit u + 1 are issued
+      // before the rescale of unit u.
+      v4i av[kMI][2], bv[2][2];
+      float4 dnv[2];      // per n-subtile: d0 / 16, d1 / 16, -1.5 * 2^23 * (d0 + d1) / 16
+      float sav[16];
+      auto load_group = [&](int gi) {
   #pragma unroll
-      for (int gi = 0; gi < kChunkGroups; ++gi) {
-        const int g = c * kChunkGroups + gi;
-        if (g < G) {   // also keeps the scheduler from interleaving groups (registers)
-          const int bl0 = 2 * gi;
-          v4i av[kMI][2];
-          float sav[kMI][16];
+        for (int mi = 0; mi < kMI; ++mi)
   #pragma unroll
-          for (int mi = 0; mi < kMI; ++mi) {
-  #pragma unroll
-            for (int bi = 0; bi < 2; ++bi) {
-              const uint4 t = *reinterpret_cast<const uint4*>(
-                  L + off_a + ((mi * kChunkBlocks + bl0 + bi) * 64) * 16);
-              av[mi][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
-            }
-            if (!kDebug) {
-  #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float4 f = *reinterpret_cast<const float4*>(
-                    L + off_sa + (gi * TM + mi * 32 + 8 * r) * 4);
-                sav[mi][4 * r + 0] = f.x; sav[mi][4 * r + 1] = f.y;
-                sav[mi][4 * r + 2] = f.z; sav[mi][4 * r + 3] = f.w;
-              }
-            }
+          for (int bi = 0; bi < 2; ++bi) {
+            const uint4 t = *reinterpret_cast<const uint4*>(
+                L + off_a + ((mi * kChunkBlocks + 2 * gi + bi) * 64) * 16);
+            av[mi][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
           }
   #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const int col = (wn * 2 + ni) * 32 + j;
-            const uint4 b0r = *reinterpret_cast<const uint4*>(
-                L + off_b[bl0] + ((ni * kChunkBlocks + bl0) * 64) * 16);
-            const uint4 b1r = *reinterpret_cast<const uint4*>(
-                L + off_b[bl0 + 1] + ((ni * kChunkBlocks + bl0 + 1) * 64) * 16);
-            const v4i bv0 = v4i{(int)b0r.x, (int)b0r.y, (int)b0r.z, (int)b0r.w};
-            const v4i bv1 = v4i{(int)b1r.x, (int)b1r.y, (int)b1r.z, (int)b1r.w};
-            float d0 = 0.f, d1 = 0.f, nc = 0.f;
-            if (!kDebug) {
-              d0 = *reinterpret_cast<const float*>(L + off_sd + (bl0 * kSdStride + ni * 32) * 4);
-              d1 = *reinterpret_cast<const float*>(L + off_sd + ((bl0 + 1) * kSdStride + ni * 32) * 4);
-              nc = *reinterpret_cast<const float*>(L + off_sb + (gi * kTN + ni * 32) * 4);
-            }
+        for (int ni = 0; ni < 2; ++ni)
   #pragma unroll
-            for (int mi = 0; mi < kMI; ++mi) {
-              const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][0], bv0, magic, 0, 0, 0);
-              const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][1], bv1, magic, 0, 0, 0);
-              if (kDebug) {
-                const int ncol = n_base + col;
+          for (int bi = 0; bi < 2; ++bi) {
+            const uint4 t = *reinterpret_cast<const uint4*>(
+                L + off_b[2 * gi + bi] + ((ni * kChunkBlocks + 2 * gi + bi) * 64) * 16);
+            bv[ni][bi] = v4i{(int)t.x, (int)t.y, (int)t.z, (int)t.w};
+          }
+      };
+      auto load_dn = [&](int gi) {
+        if (!kDebug) {
   #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                  const int mrow = (mt32 + wm * kMI + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
-                  if (mrow < M && ncol < N) {
-                    int32_t* o = acc_dbg + ((size_t)mrow * N + ncol) * nb + 2 * g;
-                    o[0] = (D0[v] - 0x4B400000) >> 4;
-                    o[1] = (D1[v] - 0x4B400000) >> 4;
-                  }
-                }
-              } else {
-  #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                  const float s = fmaf(__int_as_float(D0[v]), d0, fmaf(__int_as_float(D1[v]), d1, nc));
-                  acc[mi][ni][v] = fmaf(s, sav[mi][v], acc[mi][ni][v]);
-                }
-              }
-            }
+          for (int ni = 0; ni < 2; ++ni)
+          {
+            const float2 t = *reinterpret_cast<const float2*>(L + off_dn + (gi * kTN + ni * 32) * 8);
+            dnv[ni] = make_float4(t.x, t.y, -kMagic * (t.x + t.y), 0.f);
           }
         }
+      };
+      auto load_sa = [&](int gi, int mi, float (&s)[16]) {
+        if (!kDebug) {
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float4 f = *reinterpret_cast<const float4*>(L + off_sa + (gi * TM + mi * 32 + 8 * r) * 4);
+            s[4 * r + 0] = f.x; s[4 * r + 1] = f.y; s[4 * r + 2] = f.z; s[4 * r + 3] = f.w;
+          }
+        }
+      };
+
+      // The order below is pinned with empty asm statements that "modify"
+      // the MFMA inputs just before each issue and each unit's accumulators
+      // just after its rescale; without them the compiler hoists every MFMA
+      // of the chunk to the top, and their results no longer fit in registers.
+      // mfma_pair issues a unit's two MFMAs into d0, d1; the asm after them
+      // also "touches" c0, c1 (the previous unit's results), so that unit's
+      // rescale cannot start before this issue.
+      auto mfma_pair = [&](int mi, int ni, v16i& d0, v16i& d1, v16i& c0, v16i& c1) {
+        asm volatile("" : "+v"(av[mi][0]), "+v"(av[mi][1]), "+v"(bv[ni][0]), "+v"(bv[ni][1]));
+        d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][0], bv[ni][0], magic, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mi][1], bv[ni][1], magic, 0, 0, 0);
+        asm volatile("" : "+v"(d0), "+v"(d1), "+v"(c0), "+v"(c1));
+      };
+      v16i dc0, dc1;      // the unit being rescaled
+      load_group(0);
+      load_dn(0);
+      load_sa(0, 0, sav);
+      asm volatile("" : "+v"(av[0][0]), "+v"(av[0][1]), "+v"(bv[0][0]), "+v"(bv[0][1]));
+      dc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0][0], bv[0][0], magic, 0, 0, 0);
+      dc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[0][1], bv[0][1], magic, 0, 0, 0);
+      asm volatile("" : "+v"(dc0), "+v"(dc1));
+  #pragma unroll
+      for (int u = 0; u < kUnits; ++u) {
+        const int gi = u / kUPG, mi = (u >> 1) % kMI, ni = u & 1;
+        v16i dn0, dn1;
+        if (u + 1 < kUnits) {
+          const int u1 = u + 1;
+          const int gi1 = u1 / kUPG, mi1 = (u1 >> 1) % kMI, ni1 = u1 & 1;
+          if (u1 % kUPG == 0) load_group(gi1);
+          mfma_pair(mi1, ni1, dn0, dn1, dc0, dc1);
+        }
+        const int g = c * kChunkGroups + gi;
+        if (kDebug) {
+          const int ncol = n_base + (wn * 2 + ni) * 32 + j;
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int mrow = (mt32 + wm * kMI + mi) * kA8TileM + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (mrow < M && ncol < N && g < G) {
+              int32_t* o = acc_dbg + ((size_t)mrow * N + ncol) * nb + 2 * g;
+              o[0] = (dc0[v] - 0x4B400000) >> 4;
+              o[1] = (dc1[v] - 0x4B400000) >> 4;
+            }
+          }
+        } else {
+          const float4 d = dnv[ni];
+          const float* sv = sav;
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float s = fmaf(__int_as_float(dc0[v]), d.x, fmaf(__int_as_float(dc1[v]), d.y, d.z));
+            acc[mi][ni][v] = fmaf(s, sv[v], acc[mi][ni][v]);
+          }
+  #pragma unroll
+          for (int v = 0; v < 16; v += 4)
+            asm volatile("" : "+v"(acc[mi][ni][v]), "+v"(acc[mi][ni][v + 1]), "+v"(acc[mi][ni][v + 2]),
+                         "+v"(acc[mi][ni][v + 3]));
+        }
+        if (u + 1 < kUnits) {
+          dc0 = dn0;
+          dc1 = dn1;
+          // the scales of the next unit, when they change (read here rather
+          // than one unit ahead: one set of registers)
+          const int u1 = u + 1;
+          if (u1 % kUPG == 0) load_dn(u1 / kUPG);
+          if ((u1 & 1) == 0) load_sa(u1 / kUPG, (u1 >> 1) % kMI, sav);
+        }
+        // keep the scheduler from hoisting later units' MFMAs (each holds
+        // 32 result registers) above this unit's rescale
+        __builtin_amdgcn_sched_barrier(0);
       }
-      stage_commit(lds[(c - c0 + 1) & 1]);       // zeros past the segment
+      stage_commit(nxt);                         // past the segment: never read
+      __builtin_amdgcn_s_waitcnt(0);             // the next activation tile has landed
       __syncthreads();
+    };
+#pragma unroll 1
+    for (int c = c0; c < c1; c += 2) {
+      chunk(c, lds0, lds1);
+      if (c + 1 < c1) chunk(c + 1, lds1, lds0);
     }
   };
 
@@ -474,6 +541,7 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
       const int c1 = min(nchunks, c0 + (u1 - u));
       segment(t, c0, c1);
       u += c1 - c0;
+      if (kDebug) continue;          // block sums were written by segment()
       if (c0 == 0 && c1 == nchunks) {
         store_y(t, own);
         continue;
@@ -579,7 +647,7 @@ hipError_t launch_a8w4_gemm(const void* ws, const uint8_t* codes, const uint16_t
   // and out 163 -> 157 us; at M = 512 (544 tiles) gate 164 -> 145 us.  At
   // 896 tiles (qkv, M = 2048) it measured 6% slower, at 1088 no better and at
   // 2176 (gate, M = 2048) 10% slower, so larger counts run the plain form.
-  const bool split = !acc_debug && mp >= kA8SplitMinRows && tiles > kA8Slots &&
+  const bool split = mp >= kA8SplitMinRows && tiles > kA8Slots &&
                      tiles <= kA8Slots + kA8Slots / 2 && tiles * nchunks < (int64_t)1 << 30;
   // 64-row tiles when 128-row tiles would leave CUs idle (measured at M = 512:
   // qkv 81 -> 71 us, out 75 -> 63, down 239 -> 205; at 320..448 tiles the
@@ -603,7 +671,8 @@ hipError_t launch_a8w4_gemm(const void* ws, const uint8_t* codes, const uint16_t
                      reinterpret_cast<const uint4*>(codes), scales, y, acc_debug, (int)M, (int)N, \
                      (int)K, mtiles, ntiles, upw, partial, counters)
   if (acc_debug) {
-    if (narrow) Q4W_A8_LAUNCH(true, 2, false);
+    if (split) Q4W_A8_LAUNCH(true, 4, true);
+    else if (narrow) Q4W_A8_LAUNCH(true, 2, false);
     else Q4W_A8_LAUNCH(true, 4, false);
   } else if (split) {
     Q4W_A8_LAUNCH(false, 4, true);

@@ -119,6 +119,26 @@ def test_chunk_balanced_form(n, k):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
 
 
+def test_chunk_balanced_form_block_sums():
+    """The exact int32 block sums from the chunk-balanced form: M = 256,
+    N = 38400 (600 tiles of 128 x 128 over 512 workgroups, so chunk ranges
+    cut tiles), K = 192 (a half chunk at the end of every tile).  Every block
+    of a tile is computed by exactly one workgroup, which writes it.  Checked
+    bit-exactly on sampled columns of every column tile, all tokens."""
+    torch = torch_cuda()
+    m, n, k = 256, 38400, 192
+    codes, scales, q, d = _packed(n, k, 910)
+    x = synthetic.activations(m, k, 911)
+    acc = a8w4_debug_block_acc(dev(x, torch), codes, scales)
+    rng = np.random.default_rng(912)
+    cols = np.unique(np.concatenate([np.arange(0, n, 128), np.arange(127, n, 128),
+                                     rng.integers(0, n, 600)]))
+    got = host(acc.index_select(1, torch.as_tensor(cols, device=acc.device)))
+    del acc
+    qa, _ = a8.quantize_act(x)
+    assert np.array_equal(got, a8.block_sums(qa, q[cols]).astype(np.int32))
+
+
 def test_prepare_then_gemm_matches_one_call():
     """Quantize once, reuse for two weight matrices; bit-identical to the one-call route."""
     torch = torch_cuda()
