@@ -6,14 +6,23 @@ gate/up shape) streaming one of >= 2 GB of distinct packed weight copies, so
 the 256 MB Infinity Cache cannot serve it.  `value` is the effective
 weight-stream bandwidth of those K steps (algorithmic bytes / time).
 
-The timed region replays a HIP graph holding exactly K captured launches
-(launch-bound inner loops belong in graphs); the same K launches issued
-eagerly from Python are reported beside it.  Extra sections, each timed the
-same way, cover the rest of the path:
-  verify_down_per_M      K = 17408, N = 5120, M = 1..16 (speculative verify)
-  decode_step_64L        64 layers x {qkv, out, gate, up, down} at M = 5
+Timing.  The GPU is first run for about half a second so that its clocks
+have left their idle state (the first timed region of a cold process reads
+10-15% slow).  The timed region is the K launches issued on one stream
+between two events; an untimed batch of K launches is queued in front, so
+the GPU is already executing when the start event is reached and the host's
+launch latency is not counted as GPU time.  The region is synchronized on
+both sides.  The same K launches as one HIP graph replay are reported
+beside it: a replay carries a fixed cost of about 12 us on this runtime (its
+own start and completion), 5% of the region at K = 20, so the stream timing
+is the one that measures the GEMVs.  Longer regions (a decode step, a
+prefill pass, the A8 GEMM) replay their graph with one untimed replay in
+front.  Extra sections, each timed the same way, cover the rest of the path:
+  verify_down            K = 17408, N = 5120, M = 1..16 (speculative verify)
+  decode_step_64L        64 layers x {qkv, out, gate, up, down}: M = 5 as a
+                         320-launch graph, and M = 1, 4, 5 as one persistent launch
   a8w4_prefill           M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
-  a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048 (section "pass")
+  a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048
 plus `roofline` for the dominant kernel and `cpu_baseline` (the oracle).
 """
 
@@ -33,6 +42,7 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
 ROTATE_BYTES = 2 * 1024 ** 3  # distinct weight bytes cycled through per series
 BYTES_PER_WEIGHT = 0.5625     # 4 bits + one fp16 scale per 32 weights
+CLOCK_WARMUP_S = 0.5          # GPU time spent before anything is timed
 
 
 def log(*a):
@@ -48,17 +58,28 @@ def gemv_bytes(m, k, n):
 # timing helpers
 # --------------------------------------------------------------------------
 
-def time_region(torch, fn):
-    """Run fn() between two synchronizations, timed with events on the current stream."""
+def time_region(torch, fn, preroll=None):
+    """GPU seconds of fn(), between events on the current stream.  preroll
+    (untimed) is enqueued first so the GPU is busy when the start event is
+    reached; the region is synchronized on both sides."""
     s = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if preroll is not None:
+        preroll()
     start.record(s)
     fn()
     stop.record(s)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3
+
+
+def warm_clocks(torch, fn, seconds=CLOCK_WARMUP_S):
+    """Run fn() (untimed work) until about `seconds` of GPU time have passed."""
+    t = time_region(torch, fn)
+    reps = max(1, int(seconds / max(t, 1e-6)))
+    time_region(torch, lambda: [fn() for _ in range(reps)])
 
 
 def capture(torch, fn):
@@ -74,6 +95,11 @@ def capture(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def time_graph(torch, g, reps=1):
+    """GPU seconds of `reps` replays of g, with one untimed replay in front."""
+    return time_region(torch, lambda: [g.replay() for _ in range(reps)], preroll=g.replay) / reps
 
 
 # --------------------------------------------------------------------------
@@ -93,9 +119,11 @@ def make_copies(torch, q4w, synthetic, n, k, base_seed):
 
 
 def gemv_series(torch, q4w, copies, x, y, steps, warmup, series=1):
-    """Returns (graph seconds, eager seconds) for `steps` launches rotating over
-    copies; with series > 1 the graph of `steps` launches is timed that many
-    times and the median is returned (and the list as a third value)."""
+    """Returns (stream seconds, graph seconds) for `steps` launches rotating
+    over copies: the launches issued on the stream (an untimed batch of
+    `steps` launches queued in front), and the same launches as one HIP
+    graph replay.  With series > 1 each is timed that many times and the
+    medians are returned (and the stream times as a third value)."""
     m, k = x.shape
     n = copies[0][0].shape[0]
     ws = torch.zeros(max(q4w.gemv_ws_bytes(m, n, k, 0), 1), dtype=torch.uint8, device="cuda")
@@ -106,14 +134,16 @@ def gemv_series(torch, q4w, copies, x, y, steps, warmup, series=1):
             q4w.q4_gemv_skinny_raw(x, c, s, y, 0, ws)
 
     launches(warmup)
-    t_eager = time_region(torch, lambda: launches(steps))
+    t_stream = [time_region(torch, lambda: launches(steps), preroll=lambda: launches(steps))
+                for _ in range(series)]
     g = capture(torch, lambda: launches(steps))
     g.replay()
-    times = [time_region(torch, g.replay) for _ in range(series)]
+    t_graph = [time_graph(torch, g) for _ in range(series)]
     del g
+    med = lambda v: sorted(v)[len(v) // 2]   # noqa: E731
     if series == 1:
-        return times[0], t_eager
-    return sorted(times)[series // 2], t_eager, times
+        return t_stream[0], t_graph[0]
+    return med(t_stream), med(t_graph), t_stream
 
 
 # --------------------------------------------------------------------------
@@ -126,12 +156,14 @@ def bench_decode(torch, q4w, synthetic, steps, warmup):
     copies = make_copies(torch, q4w, synthetic, n, k, 10_000)
     x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
     y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-    tg, te = gemv_series(torch, q4w, copies, x, y, steps, warmup)
+    ws = torch.zeros(max(q4w.gemv_ws_bytes(m, n, k, 0), 1), dtype=torch.uint8, device="cuda")
+    warm_clocks(torch, lambda: [q4w.q4_gemv_skinny_raw(x, c, s, y, 0, ws) for c, s in copies])
+    ts, tg = gemv_series(torch, q4w, copies, x, y, steps, warmup)
     b = gemv_bytes(m, k, n)
     out = dict(M=m, K=k, N=n, copies=len(copies), bytes_per_launch=b,
-               t_graph_s=tg, t_eager_s=te,
-               gbs_graph=b * steps / tg / 1e9, gbs_eager=b * steps / te / 1e9,
-               us_per_launch_graph=tg / steps * 1e6, us_per_launch_eager=te / steps * 1e6)
+               t_stream_s=ts, t_graph_s=tg,
+               gbs_stream=b * steps / ts / 1e9, gbs_graph=b * steps / tg / 1e9,
+               us_per_launch_stream=ts / steps * 1e6, us_per_launch_graph=tg / steps * 1e6)
     del copies
     torch.cuda.empty_cache()
     return out
@@ -146,41 +178,54 @@ def bench_verify(torch, q4w, synthetic, steps, warmup):
         # median of three timed graph replays of `steps` launches (min and max kept)
         x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-        tg, te, ts = gemv_series(torch, q4w, copies, x, y, steps, warmup, series=3)
+        t, tg, ts = gemv_series(torch, q4w, copies, x, y, steps, warmup, series=3)
         b = gemv_bytes(m, k, n)
-        res[str(m)] = dict(gbs_graph=b * steps / tg / 1e9, gbs_eager=b * steps / te / 1e9,
-                           us_per_launch_graph=tg / steps * 1e6,
-                           us_per_launch_graph_min_max=[min(ts) / steps * 1e6, max(ts) / steps * 1e6],
-                           frac_of_peak=b * steps / tg / 1e9 / HBM_PEAK_GBS)
+        res[str(m)] = dict(gbs=b * steps / t / 1e9, us_per_launch=t / steps * 1e6,
+                           us_per_launch_min_max=[min(ts) / steps * 1e6, max(ts) / steps * 1e6],
+                           frac_of_peak=b * steps / t / 1e9 / HBM_PEAK_GBS,
+                           gbs_graph=b * steps / tg / 1e9)
     del copies
     torch.cuda.empty_cache()
     return dict(K=k, N=n, per_M=res)
 
 
-def bench_decode_step(torch, q4w, synthetic, reps, m=5):
-    """64 layers x 5 projections at M = 5, back to back on one stream."""
+def bench_decode_step(torch, q4w, synthetic, reps, ms=(5, 1, 4)):
+    """64 layers x 5 projections, back to back on one stream: at M = 5 as a
+    graph of 320 launches and as one persistent launch; at M = 1 and 4 as one
+    persistent launch (the same packed weights)."""
     from bit_quantized_weight_amd.decode import DecodeStep
-    step = DecodeStep(m)
-    torch.cuda.synchronize()
-    for _ in range(2):
-        step.run()
-    t_eager = time_region(torch, lambda: [step.run() for _ in range(reps)]) / reps
-    g = capture(torch, step.run)
-    g.replay()
-    t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
-    # the same step as one persistent launch over all 320 matmuls
-    step.plan_batched()
-    for _ in range(2):
-        step.run_batched()
-    t_batched = time_region(torch, lambda: [step.run_batched() for _ in range(reps)]) / reps
-    total = step.weight_bytes + step.io_bytes
-    out = dict(M=m, layers=len(step.layers), launches_per_step=step.launches,
-               weight_bytes_per_step=step.weight_bytes, ms_graph=t_graph * 1e3,
-               ms_eager=t_eager * 1e3, gbs_graph=total / t_graph / 1e9,
-               gbs_eager=total / t_eager / 1e9,
-               ms_batched=t_batched * 1e3, gbs_batched=total / t_batched / 1e9,
-               batched_grid=step.batch.plan.grid, batched_items=step.batch.plan.total_items)
-    del g, step
+    out = {}
+    base = None
+    for m in ms:
+        step = DecodeStep(m, weights=None if base is None else base.layers)
+        torch.cuda.synchronize()
+        total = step.weight_bytes + step.io_bytes
+        r = dict(M=m, layers=len(step.layers), weight_bytes_per_step=step.weight_bytes)
+        if base is None:
+            for _ in range(2):
+                step.run()
+            warm_clocks(torch, step.run)
+            t_eager = time_region(torch, lambda: [step.run() for _ in range(reps)], preroll=step.run) / reps
+            g = capture(torch, step.run)
+            g.replay()
+            t_graph = time_graph(torch, g, reps)
+            del g
+            r.update(launches_per_step=step.launches, ms_graph=t_graph * 1e3, ms_eager=t_eager * 1e3,
+                     gbs_graph=total / t_graph / 1e9, gbs_eager=total / t_eager / 1e9)
+        step.plan_batched()
+        for _ in range(2):
+            step.run_batched()
+        t_batched = time_region(torch, lambda: [step.run_batched() for _ in range(reps)],
+                                preroll=step.run_batched) / reps
+        r.update(ms_batched=t_batched * 1e3, gbs_batched=total / t_batched / 1e9,
+                 frac_batched=total / t_batched / 1e9 / HBM_PEAK_GBS,
+                 batched_grid=step.batch.plan.grid, batched_items=step.batch.plan.total_items)
+        out[str(m)] = r
+        if base is None:
+            base = step
+        else:
+            del step
+    del base
     torch.cuda.empty_cache()
     return out
 
@@ -188,7 +233,7 @@ def bench_decode_step(torch, q4w, synthetic, reps, m=5):
 def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
     """64 layers x 5 projections on the A8 route at M = 512, 1024 and 2048
     tokens (one packed weight set): per layer three activation quantizations
-    and five GEMMs, as a HIP graph."""
+    and four GEMMs (gate and up as one), as a HIP graph."""
     from bit_quantized_weight_amd.prefill import PrefillPass
     weights = None
     per_m = {}
@@ -197,10 +242,10 @@ def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
         weights = p.layers
         torch.cuda.synchronize()
         p.run()
-        t_eager = time_region(torch, lambda: [p.run() for _ in range(reps)]) / reps
+        t_eager = time_region(torch, lambda: [p.run() for _ in range(reps)], preroll=p.run) / reps
         g = capture(torch, p.run)
         g.replay()
-        t_graph = time_region(torch, lambda: [g.replay() for _ in range(reps)]) / reps
+        t_graph = time_graph(torch, g, reps)
         per_m[str(m)] = dict(int_ops_per_pass=p.int_ops, ms_graph=t_graph * 1e3, ms_eager=t_eager * 1e3,
                              tok_s=m / t_graph, tops=p.int_ops / t_graph / 1e12)
         layers = len(p.layers)
@@ -208,12 +253,13 @@ def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
         torch.cuda.empty_cache()
     del weights
     torch.cuda.empty_cache()
-    return dict(layers=layers, launches_per_pass=8 * layers, per_M=per_m)
+    return dict(layers=layers, launches_per_pass=7 * layers, per_M=per_m)
 
 
 def bench_prefill(torch, q4w, synthetic, reps):
-    """A8 route at M = 2048: the whole route per launch pair (activation
-    quantization + GEMM), and the GEMM alone from prepared activations."""
+    """A8 route at M = 2048, one projection (K = 5120, N = 17408): the GEMM
+    alone from prepared activations (the dominant kernel), then the whole
+    route per call (activation quantization + GEMM)."""
     wl = synthetic.WORKLOADS["prefill_a8"]
     m, k, n = wl["M"], wl["K"], wl["N"]
     w = synthetic.weights_device(n, k, synthetic.WEIGHT_SEED)
@@ -221,70 +267,129 @@ def bench_prefill(torch, q4w, synthetic, reps):
     del w
     x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
     y = torch.empty((m, n), dtype=torch.float16, device="cuda")
-    for _ in range(3):
-        q4w.a8w4_gemm(x, codes, scales, y)
-    t_route = time_region(torch, lambda: [q4w.a8w4_gemm(x, codes, scales, y) for _ in range(reps)]) / reps
     ws = q4w.a8w4_prepare(x)
-    for _ in range(3):
-        q4w.a8w4_gemm_prepared(ws, m, k, codes, scales, y)
-    t_gemm = time_region(torch, lambda: [q4w.a8w4_gemm_prepared(ws, m, k, codes, scales, y)
-                                          for _ in range(reps)]) / reps
+    gemm = lambda: q4w.a8w4_gemm_prepared(ws, m, k, codes, scales, y)   # noqa: E731
+    warm_clocks(torch, gemm)
+    t_gemm = time_region(torch, lambda: [gemm() for _ in range(reps)], preroll=gemm) / reps
+    route = lambda: q4w.a8w4_gemm(x, codes, scales, y)                   # noqa: E731
+    route()
+    t_route = time_region(torch, lambda: [route() for _ in range(reps)], preroll=route) / reps
+    t_quant = time_region(torch, lambda: [q4w.a8w4_prepare(x, ws) for _ in range(reps)],
+                          preroll=lambda: q4w.a8w4_prepare(x, ws)) / reps
     ops = 2 * m * n * k
-    return dict(M=m, K=k, N=n, ms_route=t_route * 1e3, ms_gemm=t_gemm * 1e3,
-                tok_s=m / t_route, tops_gemm=ops / t_gemm / 1e12, tops_route=ops / t_route / 1e12)
+    return dict(M=m, K=k, N=n, ms_route=t_route * 1e3, ms_gemm=t_gemm * 1e3, ms_act_quant=t_quant * 1e3,
+                one_projection_tokens_per_s=m / t_route,
+                tops_gemm=ops / t_gemm / 1e12, tops_route=ops / t_route / 1e12)
 
 
 # --------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on the host cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(synthetic, budget_s=15.0):
-    from oracle import q4
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def _timed_calls(fn, budget_s):
+    fn()                                     # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            return reps, el
+
+
+def cpu_baseline(synthetic, budget_s=4.0):
+    """The oracle, untuned, on the host: the headline GEMV with all BLAS
+    threads and with one, the verify down-projection at M = 5, and the exact
+    A8 route on a token sample of the M = 2048 projection."""
+    from oracle import a8, q4
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    threads = _blas_threads()
+    out = {}
+    # headline: decode_gate_up, M = 1
     wl = synthetic.WORKLOADS["decode_gate_up"]
     m, k, n = wl["M"], wl["K"], wl["N"]
     w = synthetic.weights(n, k, synthetic.WEIGHT_SEED)
     q, d = q4.quantize(w)          # preparation, not timed (as on the GPU)
     del w
     x = synthetic.activations(m, k, synthetic.ACT_SEED)
-    q4.matmul(x, q, d)             # warm-up
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        q4.matmul(x, q, d)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
     b = gemv_bytes(m, k, n)
-    return dict(value=b * reps / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"oracle q4.matmul (dequantize to fp64, then fp64 matvec) on the full "
-                       f"decode_gate_up matrix M={m} K={k} N={n}, {reps} calls in {el:.1f} s; "
-                       f"host has {os.cpu_count()} logical CPUs")
+    reps, el = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
+    out.update(value=b * reps / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+               sample=f"oracle q4.matmul (dequantize to fp64, then fp64 matvec) on the full "
+                      f"decode_gate_up matrix M={m} K={k} N={n}, {reps} calls in {el:.1f} s; "
+                      f"{threads} BLAS threads; host has {os.cpu_count()} logical CPUs")
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            reps1, el1 = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
+        out["single_thread"] = dict(value=b * reps1 / el1 / 1e9, unit="GB/s", cores=1,
+                                    sample=f"same, {reps1} calls in {el1:.1f} s, 1 BLAS thread")
+    del q, d
+    # verify down-projection, M = 5 (K = 17408, N = 5120)
+    wl = synthetic.WORKLOADS["verify_down"]
+    k, n, m = wl["K"], wl["N"], 5
+    w = synthetic.weights(n, k, synthetic.WEIGHT_SEED)
+    q, d = q4.quantize(w)
+    del w
+    x = synthetic.activations(m, k, synthetic.ACT_SEED)
+    reps, el = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
+    out["verify_down_m5"] = dict(value=gemv_bytes(m, k, n) * reps / el / 1e9, unit="GB/s", cores=int(threads),
+                                 sample=f"q4.matmul M={m} K={k} N={n}, {reps} calls in {el:.1f} s")
+    del q, d
+    # A8 route, M = 2048, K = 5120, N = 17408: the exact oracle on 64 of the tokens
+    wl = synthetic.WORKLOADS["prefill_a8"]
+    m, k, n = wl["M"], wl["K"], wl["N"]
+    w = synthetic.weights(n, k, synthetic.WEIGHT_SEED)
+    q, d = q4.quantize(w)
+    del w
+    tokens = 64
+    x = synthetic.activations(tokens, k, synthetic.ACT_SEED)
+    reps, el = _timed_calls(lambda: a8.prefill(x, q, d), budget_s)
+    out["a8_prefill"] = dict(value=tokens * reps / el, unit="tokens/s", cores=int(threads),
+                             tops=2 * tokens * n * k * reps / el / 1e12,
+                             sample=f"a8.prefill (int8 quantization, 160 fp64 K=32 GEMMs of exact block "
+                                    f"sums, fp64 rescale) on {tokens} tokens x K={k} x N={n}, "
+                                    f"{reps} calls in {el:.1f} s")
+    return out
 
 
 # --------------------------------------------------------------------------
 # traffic counters recorded under profiles/ (valid only for the same kernel source)
 # --------------------------------------------------------------------------
 
-def kernel_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in ("q4_gemv.hip", "q4w_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "bit_quantized_weight_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    path = os.path.join(ROOT, "profiles", "skinny_decode_gate_up_traffic.json")
+def kernel_source_hash():
+    return source_hash(("q4_gemv.hip", "q4w_internal.h"))
+
+
+def a8_source_hash():
+    return source_hash(("a8w4.hip", "q4w_internal.h"))
+
+
+def recorded_traffic(name, current_hash):
+    path = os.path.join(ROOT, "profiles", name)
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != current_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -299,6 +404,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sections", default="decode,verify,step,prefill,pass",
                     help="comma list of extra sections (decode is always run)")
+    ap.add_argument("--only", default=None,
+                    help="run only this section (decode, verify, step, prefill, pass) and print its "
+                         "result; for profiling one kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -316,7 +424,6 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     q4w.lib()  # fail loudly if the HIP library is missing
-    sections = set(args.sections.split(","))
 
     if args.copy_calibration:
         src = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
@@ -326,30 +433,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+
+    if args.only:
+        fn = {"decode": lambda: bench_decode(torch, q4w, synthetic, args.steps, args.warmup),
+              "verify": lambda: bench_verify(torch, q4w, synthetic, max(args.steps // 3, 50), args.warmup),
+              "step": lambda: bench_decode_step(torch, q4w, synthetic, reps=10),
+              "prefill": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5)),
+              "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
+
+    sections = set(args.sections.split(","))
     log(f"[bench] decode_gate_up: {args.steps} steps, {args.warmup} warmup")
     dec = bench_decode(torch, q4w, synthetic, args.steps, args.warmup)
-    log(f"[bench] decode_gate_up: {dec['gbs_graph']:.0f} GB/s graph, {dec['gbs_eager']:.0f} GB/s eager")
+    log(f"[bench] decode_gate_up: {dec['gbs_stream']:.0f} GB/s, {dec['gbs_graph']:.0f} GB/s as one graph")
     extra = {}
     if "verify" in sections:
         extra["verify_down"] = bench_verify(torch, q4w, synthetic, max(args.steps // 3, 50), args.warmup)
-        log("[bench] verify_down:", {mm: round(v["gbs_graph"]) for mm, v in extra["verify_down"]["per_M"].items()})
+        log("[bench] verify_down:", {mm: round(v["gbs"]) for mm, v in extra["verify_down"]["per_M"].items()})
     if "step" in sections:
         extra["decode_step_64L"] = bench_decode_step(torch, q4w, synthetic, reps=10)
-        log(f"[bench] decode_step_64L: {extra['decode_step_64L']['ms_graph']:.3f} ms graph")
+        log("[bench] decode_step_64L:",
+            {mm: round(v["ms_batched"], 3) for mm, v in extra["decode_step_64L"].items()},
+            f"ms batched; M=5 graph {extra['decode_step_64L']['5']['ms_graph']:.3f} ms")
     if "prefill" in sections:
         extra["a8w4_prefill"] = bench_prefill(torch, q4w, synthetic, reps=20)
-        log(f"[bench] a8w4_prefill: route {extra['a8w4_prefill']['ms_route']:.3f} ms "
-            f"({extra['a8w4_prefill']['tok_s']:.0f} tok/s), GEMM {extra['a8w4_prefill']['ms_gemm']:.3f} ms")
+        p = extra["a8w4_prefill"]
+        log(f"[bench] a8w4_prefill: GEMM {p['ms_gemm']:.3f} ms, route {p['ms_route']:.3f} ms, "
+            f"act quant {p['ms_act_quant']:.4f} ms")
     if "pass" in sections:
         extra["a8w4_prefill_pass_64L"] = bench_prefill_pass(torch, q4w, synthetic, reps=3)
         for m_, r_ in extra["a8w4_prefill_pass_64L"]["per_M"].items():
             log(f"[bench] a8w4_prefill_pass_64L M={m_}: {r_['ms_graph']:.2f} ms ({r_['tok_s']:.0f} tok/s)")
 
     steps = args.steps
-    t = dec["t_graph_s"]
+    t = dec["t_stream_s"]
     b = dec["bytes_per_launch"]
     achieved = b / (t / steps) / 1e9
-    traffic = recorded_traffic()
     result = {
         "metric": "effective weight-stream GB/s (% of HBM peak) at M=1..5; A8W4 prefill tok/s",
         "value": round(b * steps / t / 1e9, 2),
@@ -365,12 +485,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_gate_up", "M": dec["M"], "K": dec["K"], "N": dec["N"],
                    "weight_format": "4-bit codes, fp16 scale per 32 weights",
-                   "weight_copies_rotated": dec["copies"], "timing": "HIP graph of K launches"},
+                   "weight_copies_rotated": dec["copies"],
+                   "timing": "K launches on one stream between two events, an untimed batch of K "
+                             "launches queued in front, after clock warm-up"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-        "eager": {"gbs": round(dec["gbs_eager"], 2), "us_per_launch": round(dec["us_per_launch_eager"], 3)},
-        "us_per_launch": round(dec["us_per_launch_graph"], 3),
+                     "traffic": recorded_traffic("skinny_decode_gate_up_traffic.json", kernel_source_hash())},
+        "graph": {"gbs": round(dec["gbs_graph"], 2), "us_per_launch": round(dec["us_per_launch_graph"], 3),
+                  "note": "the same K launches as one HIP graph replay, which adds a fixed cost per replay"},
+        "us_per_launch": round(dec["us_per_launch_stream"], 3),
         "kernel_source_hash": kernel_source_hash(),
     }
     result.update(extra)
@@ -378,8 +501,10 @@ def main():
         p = extra["a8w4_prefill"]
         result["a8w4_prefill"]["roofline"] = {
             "bound": "mfma", "achieved": round(p["tops_gemm"], 2), "peak": INT8_PEAK_TOPS,
-            "unit": "TOP/s", "frac": round(p["tops_gemm"] / INT8_PEAK_TOPS, 4), "traffic": None,
-            "kernel": "a8w4 int8 GEMM (activations prepared once, timed per launch)"}
+            "unit": "TOP/s", "frac": round(p["tops_gemm"] / INT8_PEAK_TOPS, 4),
+            "traffic": recorded_traffic("a8w4_prefill_gemm_traffic.json", a8_source_hash()),
+            "kernel": "a8w4 int8 GEMM (activations prepared once, timed per launch)",
+            "kernel_source_hash": a8_source_hash()}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(synthetic)

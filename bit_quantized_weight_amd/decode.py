@@ -21,10 +21,12 @@ from . import binding, synthetic
 class DecodeStep:
     """Packed weights of all layers plus the per-projection activation/output buffers."""
 
-    def __init__(self, m, layers=synthetic.N_LAYERS, device="cuda", keep_rows=None):
+    def __init__(self, m, layers=synthetic.N_LAYERS, device="cuda", keep_rows=None, weights=None):
         """keep_rows: optional {(layer, proj_index): row_index_array} whose fp32
         weight rows are copied to the host before the fp32 matrix is freed
-        (for spot checks against a CPU reference)."""
+        (for spot checks against a CPU reference).  weights: optional packed
+        per-layer [(codes, scales)] in LAYER_PROJECTIONS order, e.g. another
+        DecodeStep's ``layers`` (the same weights at another M)."""
         import torch
         self.m = m
         self.layers = []
@@ -33,12 +35,15 @@ class DecodeStep:
         for layer in range(layers):
             projs = []
             for pi, (_, k, n) in enumerate(synthetic.LAYER_PROJECTIONS):
-                w = synthetic.weights_device(n, k, synthetic.layer_weight_seed(layer, pi), device=device)
-                if keep_rows and (layer, pi) in keep_rows:
-                    idx = torch.as_tensor(keep_rows[(layer, pi)], device=device)
-                    self.kept[(layer, pi)] = w.index_select(0, idx).cpu().numpy()
-                projs.append(binding.pack(w))
-                del w
+                if weights is not None:
+                    projs.append(weights[layer][pi])
+                else:
+                    w = synthetic.weights_device(n, k, synthetic.layer_weight_seed(layer, pi), device=device)
+                    if keep_rows and (layer, pi) in keep_rows:
+                        idx = torch.as_tensor(keep_rows[(layer, pi)], device=device)
+                        self.kept[(layer, pi)] = w.index_select(0, idx).cpu().numpy()
+                    projs.append(binding.pack(w))
+                    del w
                 self.weight_bytes += n * k * 9 // 16
             self.layers.append(projs)
         self.xs = [synthetic.activations_device(m, k, synthetic.ACT_SEED + pi, device=device)
