@@ -20,8 +20,14 @@ What it computes (NumPy, float64 wherever the pages leave precision open):
   rescale.  Source: "Qwen3.8-27B on RTX 4090: 5,000 tok/s Prefill
   Reproduced" (page 5), section "Why the A8 artifact matters".
 
+* ``attn`` -- the decode-time attention read of a K/V cache held in the same
+  4-bit block format: softmax(q . K^T / sqrt(D)) V over the visible cache
+  positions, grouped query heads.  Source: page 3, the architecture and
+  bandwidth paragraphs (16 full-attention layers with a 4-bit K/V cache
+  whose reads grow with the context).
+
 Every reading of an open point is listed in the docstring of the function
 that takes it.  Parity pins live in ``tests/test_oracle_*.py``.
 """
 
-from . import q4, a8  # noqa: F401
+from . import q4, a8, attn  # noqa: F401

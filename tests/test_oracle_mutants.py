@@ -192,3 +192,56 @@ def test_a8_group_index_mutant_caught():
     qa, sa = a8.quantize_act(x)
     with pytest.raises(AssertionError):
         pins.pin_a8_exact(a8_matmul_group_index, qa, sa, q, d)
+
+
+# ---- attention-read mutants -------------------------------------------------
+
+def _attn_mutant(scale=None, vis_shift=0, head_of=None, subtract_max=True, swap_kv=False, normalize=True):
+    """A copy of the attention oracle with one plausible slip."""
+    def fn(q, k_codes, k_scales, v_codes, v_scales, n_kv_heads):
+        from oracle import attn
+        q64 = np.asarray(q, dtype=np.float16).astype(np.float64)
+        m_count, n_q, d = q64.shape
+        group = n_q // n_kv_heads
+        k = attn.dequantize_cache(k_codes, k_scales, n_kv_heads)
+        v = attn.dequantize_cache(v_codes, v_scales, n_kv_heads)
+        if swap_kv:
+            k, v = v, k
+        t = k.shape[0]
+        out = np.zeros((m_count, n_q, d))
+        for m in range(m_count):
+            n_vis = max(1, t - m_count + m + 1 + vis_shift)
+            for h in range(n_q):
+                g = head_of(h, group, n_kv_heads) if head_of else h // group
+                s = k[:n_vis, g, :] @ q64[m, h] * (scale(d) if scale else 1 / np.sqrt(d))
+                with np.errstate(over="ignore", invalid="ignore"):
+                    p = np.exp(s - np.max(s)) if subtract_max else np.exp(s)
+                    if normalize:
+                        p = p / np.sum(p)
+                out[m, h] = p @ v[:n_vis, g, :]
+        return out
+    return fn
+
+
+ATTN_MUTANTS = {
+    "scale 1/D": _attn_mutant(scale=lambda d: 1.0 / d),
+    "sees one row fewer": _attn_mutant(vis_shift=-1),
+    "sees one row more": _attn_mutant(vis_shift=+1),
+    "head h % H_kv": _attn_mutant(head_of=lambda h, g, nkv: h % nkv),
+    "no max subtracted": _attn_mutant(subtract_max=False),
+    "K and V swapped": _attn_mutant(swap_kv=True),
+    "weights not normalized": _attn_mutant(normalize=False),
+}
+
+
+@pytest.mark.parametrize("name", list(ATTN_MUTANTS))
+def test_attention_mutants_caught(name):
+    from test_oracle_attn import ALL_PINS
+    fn = ATTN_MUTANTS[name]
+    caught = 0
+    for pin in ALL_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin catches the mutant '{name}'"
