@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     Batch,
     Q4WError,
     a8_quantize_act,
+    attn_decode,
+    attn_decode_ws_bytes,
     a8w4_debug_block_acc,
     a8w4_gemm,
     a8w4_gemm_prepared,

@@ -65,6 +65,10 @@ def lib():
     L.q4_gemv_skinny.restype = i32
     L.q4_gemv_skinny_noalloc.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, vp]
     L.q4_gemv_skinny_noalloc.restype = i32
+    L.q4_attn_decode_ws_bytes.argtypes = [i32, i32, i32, i32, i64]
+    L.q4_attn_decode_ws_bytes.restype = sz
+    L.q4_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, vp, sz, vp]
+    L.q4_attn_decode.restype = i32
     L.a8_quantize_act.argtypes = [vp, i64, i64, vp, vp, vp]
     L.a8_quantize_act.restype = i32
     L.a8w4_ws_bytes.argtypes = [i64, i64]
@@ -199,6 +203,36 @@ def gemv_noalloc(x, codes, scales, y, split_k=0):
     _check("q4_gemv_skinny_noalloc", lib().q4_gemv_skinny_noalloc(
         _ptr(x), _ptr(codes), _ptr(scales), _ptr(y), m, n, k, split_k, _stream()))
     return y
+
+
+def attn_decode_ws_bytes(m, n_q_heads, n_kv_heads, head_dim, t):
+    return lib().q4_attn_decode_ws_bytes(m, n_q_heads, n_kv_heads, head_dim, t)
+
+
+def attn_decode(q, k_codes, k_scales, v_codes, v_scales, n_kv_heads, out=None, ws=None):
+    """Attention read of a 4-bit K/V cache: q fp16 [M, H_q, D]; caches as
+    q4_pack output of the [T, H_kv * D] rows (codes uint8, scales fp16)
+    -> fp16 o [M, H_q, D]."""
+    import torch
+    _need(q, torch.float16, "q")
+    for t, dt, name in ((k_codes, torch.uint8, "k_codes"), (v_codes, torch.uint8, "v_codes"),
+                        (k_scales, torch.float16, "k_scales"), (v_scales, torch.float16, "v_scales")):
+        _need(t, dt, name)
+    m, hq, d = q.shape
+    t_len = k_codes.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out")
+    _need_shape(out, q.shape, "out")
+    nb = attn_decode_ws_bytes(m, hq, n_kv_heads, d, t_len)
+    if ws is None:
+        ws = _workspace(nb, q.device, "attn")
+    else:
+        _need(ws, torch.uint8, "ws")
+    _check("q4_attn_decode", lib().q4_attn_decode(
+        _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out),
+        m, hq, n_kv_heads, d, t_len, _ptr(ws), ws.numel() if ws is not None else 0, _stream()))
+    return out
 
 
 def a8_quantize_act(x):

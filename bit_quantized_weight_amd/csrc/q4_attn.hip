@@ -1,0 +1,405 @@
+// q4_attn_decode: the decode-time attention read of a 4-bit K/V cache.
+//
+// Page 3 ("Qwen3.8-27B at 256K on a 24GB RTX PRO 4000 SFF"): 16 of the 64
+// layers are full-attention layers whose K/V cache, held with 4-bit K and V,
+// grows with the context (roughly 4.25 GiB at 256K), and those K/V reads are
+// what takes decode from about 50 tok/s to 12.61 tok/s at a 261.5K-token
+// cache.  For each of the M query tokens of a step (the last M cache
+// positions: the target token and its drafts) and each query head h:
+//   o[m, h] = sum_t softmax_t(q[m, h] . K[t, g] / sqrt(D)) V[t, g],  g = h / G,
+// over the cache positions t <= T - M + m.  K and V are token-major rows of
+// H_kv * D values in the weights' 32-element 4-bit block format.
+//
+// gfx950 design (bound by streaming the cache from HBM):
+//  * One workgroup (8 waves) per (K/V head g, slice of the keys); a wave
+//    takes 32-key tiles of its slice in turn and keeps its own running max,
+//    sum and output (flash-decoding).  The R = M * G query rows of head g
+//    are the 32 columns of every matrix product (rows past R are zero).
+//  * Scores: S^T[t, r] = K[t, :] . Q[r, :] on v_mfma_f32_32x32x16_f16.  A
+//    lane loads its key's 64 bytes of codes (half a head row) and the 4
+//    block scales, and dequantizes one code word per product into fp16
+//    (magic-exponent nibble unpack, exact integer codes, one rounding of
+//    q * d); Q^T sits in LDS in the matching d order.  A lane then holds 16
+//    keys of one query row: the row max and sum need one cross-half swap.
+//  * Softmax in base 2, in fp32, with a lazy running max: the output is
+//    rescaled only when some row's max grows by more than 8 (p <= 256).
+//  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  Each lane dequantizes its
+//    key's V half-row into a wave-private LDS tile; the product reads that
+//    tile transposed (8 keys of one channel per lane); P^T comes from the
+//    scores' registers through two v_permlane32_swap per 16 keys.
+//  * The 8 waves' partial results are combined in LDS, each workgroup writes
+//    one partial (rows < R only), and a second kernel merges the slices.
+
+#include "q4w_internal.h"
+#include <hip/hip_fp16.h>
+
+namespace q4w {
+namespace {
+
+constexpr int kD = kAttnHeadDim;          // head dimension (256)
+constexpr int kTileKeys = 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVRow = 528;                // bytes per dequantized V row in LDS (512 + pad)
+constexpr float kNegBig = -1.0e30f;       // running-max start (finite: no inf - inf)
+constexpr float kRescaleGap = 8.0f;       // base-2 growth of the max that forces a rescale
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+struct AttnLds {
+  uint4 qt[16 * 64];                          // Q^T B operands: [product c][lane]
+  unsigned char v[kWaves][kTileKeys * kVRow]; // per-wave dequantized V tile, [key][slot]
+};
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 8 codes of one 32-bit word (elements e0..e7) times the block scale, as
+// fp16 pairs in the order (e0, e4), (e1, e5), (e2, e6), (e3, e7).
+// (w & 0x000F000F) ^ 0x64086408 is the fp16 pair (1024 + u) with u = q + 8;
+// odd nibbles sit 4 bits higher and take the exponent of 64 instead.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, h2 d2) {
+  const uint32_t w8 = w >> 8;
+  const h2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+  const h2 q0 = as_h2((w & 0x000F000Fu) ^ 0x64086408u) - c1032;    // exact codes
+  const h2 q1 = as_h2((w & 0x00F000F0u) ^ 0x54805480u) - c72;
+  const h2 q2 = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) - c1032;
+  const h2 q3 = as_h2((w8 & 0x00F000F0u) ^ 0x54805480u) - c72;
+  return make_uint4(as_u32(q0 * d2), as_u32(q1 * d2), as_u32(q2 * d2), as_u32(q3 * d2));
+}
+
+__device__ __forceinline__ h8 as_h8(uint4 v) { return __builtin_bit_cast(h8, v); }
+
+// lanes 32..63 of a <-> lanes 0..31 of b
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// ---- kernel 1: one partial result per (K/V head, key slice) ---------------
+// grid (S, H_kv), 8 waves.  Slice s covers key tiles [s * tps, (s + 1) * tps).
+// part_o: [S][H_kv][R][D] fp32, part_ml: [S][H_kv][R][2] (base-2 max, sum).
+__global__ void __launch_bounds__(kThreads)
+attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+                    const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
+                    const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
+                    float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
+  __shared__ AttnLds lds;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane & 31;                 // query row of this lane (a matrix column)
+  const int hh = lane >> 5;                // half: keys 4hh.. of each group of 8, d half
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int R = M * G;
+  const int ntiles = (T + kTileKeys - 1) / kTileKeys;
+  const int tile0 = split * tps;
+  const int tile1 = min(ntiles, tile0 + tps);
+
+  // ---- Q^T into LDS: entry (c, lane') holds Q[r', 128 h' + 8 c + (0,4,1,5,2,6,3,7)]
+  for (int e = tid; e < 16 * 64; e += kThreads) {
+    const int c = e >> 6, l2 = e & 63;
+    const int r2 = l2 & 31, h2i = l2 >> 5;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (r2 < R) {
+      const int m = r2 / G, hq = g * G + r2 % G;
+      const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)m * Hq + hq) * kD + 128 * h2i + 8 * c);
+      o.x = (w.x & 0xFFFFu) | (w.z << 16);          // (e0, e4)
+      o.y = (w.x >> 16) | (w.z & 0xFFFF0000u);      // (e1, e5)
+      o.z = (w.y & 0xFFFFu) | (w.w << 16);          // (e2, e6)
+      o.w = (w.y >> 16) | (w.w & 0xFFFF0000u);      // (e3, e7)
+    }
+    lds.qt[e] = o;
+  }
+  __syncthreads();
+
+  // ---- cache rows: key t's codes for head g are bytes [g*128, g*128+128) of its row
+  const int row_codes = Hkv * kD / 2;           // bytes per cache row
+  const int row_scales = Hkv * kD / kBlock;     // fp16 per cache row
+  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)k_codes, 0, T * row_codes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)v_codes, 0, T * row_codes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)k_scales, 0, T * row_scales * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)v_scales, 0, T * row_scales * 2, kRsrcWord3);
+  const uint32_t lane_codes = (uint32_t)(g * (kD / 2) + 64 * hh);      // + key * row_codes
+  const uint32_t lane_scales = (uint32_t)((g * (kD / kBlock) + 4 * hh) * 2);
+
+  uint4 kc[4], vc[4];         // this lane's 64 code bytes of K and of V
+  v2u ksc, vsc;               // its 4 block scales of K and of V (fp16 x 4)
+  auto load_k = [&](int tile) {
+    const int key = tile * kTileKeys + r;
+    const bool live = tile < tile1 && key < T;
+    const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
+    const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rkc, oc, 16 * i, 0);
+      kc[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    ksc = __builtin_amdgcn_raw_buffer_load_b64(rks, os, 0, 0);
+  };
+  auto load_v = [&](int tile) {
+    const int key = tile * kTileKeys + r;
+    const bool live = tile < tile1 && key < T;
+    const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
+    const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 16 * i, 0);
+      vc[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    vsc = __builtin_amdgcn_raw_buffer_load_b64(rvs, os, 0, 0);
+  };
+  auto scale2 = [](v2u s, int b) {          // block b (0..3) of the lane's 4 scales, as a pair
+    const uint32_t w = b < 2 ? s[0] : s[1];
+    const uint32_t h = (b & 1) ? (w >> 16) : (w & 0xFFFFu);
+    return as_h2(h | (h << 16));
+  };
+  auto word = [](const uint4 (&c)[4], int i) {
+    const uint4 v = c[i >> 2];
+    const int j = i & 3;
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+  };
+
+  // the last position query row r may see (rows past R: every key)
+  const int lim = r < R ? T - M + r / G : T - 1;
+  const float c2 = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(D)
+
+  f16v o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+
+  unsigned char* vt = lds.v[wave];
+  // V tile transposed read: lane (d, hh) takes channel d = 32 dt + (lane & 31)
+  // of keys 16 c' + 8 hh + j; the channel's slot inside its group of 8 is
+  // (0, 2, 4, 6, 1, 3, 5, 7)[d % 8] (the dequantized pair order).
+  const int dl = lane & 31;
+  const int slot = 8 * (dl >> 3) + (((dl & 3) << 1) | ((dl >> 2) & 1));
+  const unsigned char* vread = vt + (8 * hh) * kVRow + 2 * slot;
+
+  int tile = tile0 + wave;
+  if (tile < tile1) {
+    load_k(tile);
+    load_v(tile);
+  }
+#pragma unroll 1
+  for (; tile < tile1; tile += kWaves) {
+    const int t0 = tile * kTileKeys;
+    // ---- V: dequantize this lane's half row into the wave's LDS tile ------
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint4 p = dequant8(word(vc, c), scale2(vsc, c >> 2));
+      *reinterpret_cast<uint4*>(vt + r * kVRow + 256 * hh + 16 * c) = p;
+    }
+    load_v(tile + kWaves);                        // next tile of this wave (past the end: zeros)
+
+    // ---- scores S^T[t, r] ---------------------------------------------------
+    f16v s = {};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint4 a = dequant8(word(kc, c), scale2(ksc, c >> 2));
+      const uint4 b = lds.qt[c * 64 + lane];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), s, 0, 0, 0);
+    }
+    load_k(tile + kWaves);
+
+    // ---- softmax (base 2), lazy running max -------------------------------
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = s[v] * c2;
+    if (t0 + kTileKeys - 1 > T - M) {              // the tile reaches past some row's limit
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (t > lim) sv[v] = -__builtin_inff();
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleGap) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_run);
+      l_run += p[v];
+    }
+    // P^T as the B operand of two 16-key products: lane (r, hh) needs keys
+    // 16 c' + 8 hh + 0..7; it holds keys 8 i + 4 hh + 0..3 (i = 0..3).
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const h2 t2 = {(_Float16)p[2 * i], (_Float16)p[2 * i + 1]};
+      pk[i] = as_u32(t2);
+    }
+    swap32(pk[0], pk[2]);
+    swap32(pk[1], pk[3]);
+    swap32(pk[4], pk[6]);
+    swap32(pk[5], pk[7]);
+
+    // ---- O^T[d, r] += V^T[d, t] P^T[t, r] ---------------------------------
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      const uint4 bb = make_uint4(pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        h8 a;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          a[j] = *reinterpret_cast<const _Float16*>(vread + (16 * cp + j) * kVRow + 64 * dt);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, as_h8(bb), o[dt], 0, 0, 0);
+      }
+    }
+  }
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  // ---- combine the 8 waves in LDS (the V tiles are free now) ----------------
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&lds.v[0][0]);    // [wave][idx][lane] float4s + max
+  float* mxs = red + 4 * 32 * 64 * 4;                     // after 4 waves' outputs: [wave][32]
+  if (hh == 0) mxs[wave * 32 + r] = m_run;
+  __syncthreads();
+  float m_all = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) m_all = fmaxf(m_all, mxs[w * 32 + r]);
+  {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_all);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    l_run *= alpha;
+  }
+  float* lsum = mxs + kWaves * 32;                        // [wave][64]
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half) {
+      float4* dst = reinterpret_cast<float4*>(red) + (size_t)(wave - half) * 32 * 64;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        dst[i * 64 + lane] = make_float4(o[i >> 2][4 * (i & 3)], o[i >> 2][4 * (i & 3) + 1],
+                                         o[i >> 2][4 * (i & 3) + 2], o[i >> 2][4 * (i & 3) + 3]);
+      lsum[(wave - half) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float4* src = reinterpret_cast<const float4*>(red) + (size_t)wave * 32 * 64;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float4 f = src[i * 64 + lane];
+        o[i >> 2][4 * (i & 3)] += f.x;
+        o[i >> 2][4 * (i & 3) + 1] += f.y;
+        o[i >> 2][4 * (i & 3) + 2] += f.z;
+        o[i >> 2][4 * (i & 3) + 3] += f.w;
+      }
+      l_run += lsum[wave * 64 + lane];
+    }
+  }
+
+  // ---- wave 0 writes this slice's partial (rows < R) -------------------------
+  if (wave == 0 && r < R) {
+    const size_t row = ((size_t)split * Hkv + g) * R + r;
+    float* po = part_o + row * kD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)     // d = 32 dt + 8 i + 4 hh + (0..3)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * i + 4 * hh) =
+            make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
+    if (hh == 0) {
+      part_ml[2 * row] = m_all;
+      part_ml[2 * row + 1] = l_run;
+    }
+  }
+}
+
+// ---- kernel 2: merge the slices -------------------------------------------
+// grid (H_kv * R), one thread per channel.
+__global__ void __launch_bounds__(kD)
+attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                  uint16_t* __restrict__ out, int M, int Hq, int Hkv, int S) {
+  const int G = Hq / Hkv;
+  const int R = M * G;
+  const int g = blockIdx.x / R;
+  const int r = blockIdx.x - g * R;
+  const int d = threadIdx.x;
+  float mmax = kNegBig;
+  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, part_ml[2 * (((size_t)s * Hkv + g) * R + r)]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const size_t row = ((size_t)s * Hkv + g) * R + r;
+    const float w = __builtin_amdgcn_exp2f(part_ml[2 * row] - mmax);
+    l += part_ml[2 * row + 1] * w;
+    acc += part_o[row * kD + d] * w;
+  }
+  const int m = r / G, hq = g * G + r % G;
+  out[((size_t)m * Hq + hq) * kD + d] = __half_as_ushort(__float2half_rn(acc / l));
+}
+
+}  // namespace
+
+int attn_splits(int M, int Hq, int Hkv, int64_t T) {
+  (void)M;
+  (void)Hq;
+  const int64_t ntiles = (T + kTileKeys - 1) / kTileKeys;
+  // about one 8-wave workgroup per CU (256), each wave with at least one tile
+  int64_t s = (ntiles + kWaves - 1) / kWaves;
+  const int64_t cap = Hkv >= 256 ? 1 : 256 / Hkv;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t attn_ws_bytes(int M, int Hq, int Hkv, int64_t T) {
+  const int S = attn_splits(M, Hq, Hkv, T);
+  const size_t rows = (size_t)S * Hkv * M * (Hq / Hkv);
+  return ((rows * kD * sizeof(float) + 255) & ~(size_t)255) + rows * 2 * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                              const uint8_t* v_codes, const uint16_t* v_scales, uint16_t* out, int M,
+                              int Hq, int Hkv, int64_t T, void* ws, hipStream_t s) {
+  const int S = attn_splits(M, Hq, Hkv, T);
+  const int64_t ntiles = (T + kTileKeys - 1) / kTileKeys;
+  const int tps = (int)((ntiles + S - 1) / S);
+  const size_t rows = (size_t)S * Hkv * M * (Hq / Hkv);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                            ((rows * kD * sizeof(float) + 255) & ~(size_t)255));
+  hipLaunchKernelGGL(attn_partial_kernel, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
+                     v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(Hkv * M * (Hq / Hkv)), dim3(kD), 0, s, part_o, part_ml, out, M,
+                     Hq, Hkv, S);
+  return hipGetLastError();
+}
+
+}  // namespace q4w

@@ -248,6 +248,38 @@ int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc, 
   return hip_status(q4w::launch_a8w4_gemm(ws, codes, nullptr, nullptr, acc, M, N, K, stream));
 }
 
+// Shape checks of the attention read (no pointers): negative status or OK.
+static int attn_shape(int M, int n_q_heads, int n_kv_heads, int head_dim, int64_t T) {
+  if (M < 1 || n_q_heads < 1 || n_kv_heads < 1 || T < 0) return Q4W_ERR_INVALID_ARG;
+  if (head_dim != q4w::kAttnHeadDim || n_q_heads % n_kv_heads != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)M * (n_q_heads / n_kv_heads) > q4w::kAttnMaxRows) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (T < M) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  // cache rows are addressed with 32-bit byte offsets
+  if (T * (int64_t)n_kv_heads * (head_dim / 2) >= (int64_t(1) << 31)) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  return Q4W_OK;
+}
+
+size_t q4_attn_decode_ws_bytes(int M, int n_q_heads, int n_kv_heads, int head_dim, int64_t T) {
+  if (attn_shape(M, n_q_heads, n_kv_heads, head_dim, T) != Q4W_OK) return 0;
+  return q4w::attn_ws_bytes(M, n_q_heads, n_kv_heads, T);
+}
+
+int q4_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                   const uint8_t* v_codes, const uint16_t* v_scales, uint16_t* o, int M,
+                   int n_q_heads, int n_kv_heads, int head_dim, int64_t T, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  const int st = attn_shape(M, n_q_heads, n_kv_heads, head_dim, T);
+  if (st != Q4W_OK) return st;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o) return Q4W_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_scales, 8) ||
+      !aligned(v_scales, 8) || !aligned(o, 2))
+    return Q4W_ERR_MISALIGNED;
+  if (!ws || ws_bytes < q4w::attn_ws_bytes(M, n_q_heads, n_kv_heads, T)) return Q4W_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return Q4W_ERR_MISALIGNED;
+  return hip_status(q4w::launch_attn_decode(q, k_codes, k_scales, v_codes, v_scales, o, M, n_q_heads,
+                                            n_kv_heads, T, ws, stream));
+}
+
 const char* q4w_status_str(int status) {
   switch (status) {
     case Q4W_OK: return "OK";

@@ -98,6 +98,15 @@ int batched_grid(int M, bool quad, int64_t total_items);
 hipError_t launch_batched(int M, bool quad, const void* ws, int count, int total_items, int grid,
                           hipStream_t s);
 
+// ---- attention read of a 4-bit K/V cache (decode) ---------------------------
+constexpr int kAttnHeadDim = 256;   // head dimension the kernel is built for
+constexpr int kAttnMaxRows = 32;    // M * (H_q / H_kv): query rows of one K/V head
+int attn_splits(int M, int Hq, int Hkv, int64_t T);
+size_t attn_ws_bytes(int M, int Hq, int Hkv, int64_t T);
+hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                              const uint8_t* v_codes, const uint16_t* v_scales, uint16_t* out, int M,
+                              int Hq, int Hkv, int64_t T, void* ws, hipStream_t s);
+
 // ---- A8 prefill -----------------------------------------------------------
 constexpr int kA8TileM = 32;      // rows per MFMA tile of the private activation layout
 

@@ -191,6 +191,40 @@ int a8w4_debug_block_acc(const uint16_t* x, const uint8_t* codes, int32_t* acc,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * q4_attn_decode: the attention read of one layer's 4-bit K/V cache during
+ *   decode and speculative verification.  "Qwen3.8-27B at 256K on a 24GB RTX
+ *   PRO 4000 SFF" (page 3): 16 of the 64 layers keep a conventional K/V
+ *   cache, held with 4-bit K and V, whose reads grow with the context (the
+ *   architecture and bandwidth paragraphs).  For each of the M query tokens
+ *   (the last M cache positions: the target token and its drafted tokens)
+ *   and each query head h,
+ *     o[m, h, :] = sum_t softmax_t(q[m, h, :] . K[t, g, :] / sqrt(D)) V[t, g, :]
+ *   over t = 0 .. T - M + m, with g = h / (H_q / H_kv).
+ *   Cache layout (the pages name 4-bit K and V but no layout; this is the
+ *   reading used): per layer, K and V are each token-major [T, H_kv * D] in
+ *   the weight format above (32-element blocks along the head dimension):
+ *     k_codes, v_codes   uint8 [T, H_kv * D / 2], 16-byte aligned;
+ *     k_scales, v_scales fp16 [T, H_kv * D / 32], 8-byte aligned;
+ *   i.e. q4_pack of the fp32 rows [T, H_kv * D] (a step appends its tokens
+ *   by packing their rows in place).
+ *   q  [M, H_q, D] fp16, 16-byte aligned.  o [M, H_q, D] fp16 (RNE of an
+ *   fp32 result), 2-byte aligned.  The kernel dequantizes K and V to fp16
+ *   (one rounding of q * d), accumulates scores and outputs in fp32 and
+ *   takes the softmax in fp32.
+ *   head_dim must be 256; H_q % H_kv == 0; M * (H_q / H_kv) <= 32; M <= T;
+ *   T * H_kv * 128 < 2^31 (else UNSUPPORTED_SHAPE).  M, H_q, H_kv < 1 or
+ *   T < 0: INVALID_ARG.
+ *   ws: at least q4_attn_decode_ws_bytes(...) bytes, 256-byte aligned (the
+ *   partial results of the key slices, merged by a second kernel; results
+ *   are deterministic).  Calls sharing a workspace must not overlap.
+ */
+size_t q4_attn_decode_ws_bytes(int M, int n_q_heads, int n_kv_heads, int head_dim, int64_t T);
+int q4_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
+                   const uint8_t* v_codes, const uint16_t* v_scales, uint16_t* o, int M,
+                   int n_q_heads, int n_kv_heads, int head_dim, int64_t T, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
  * Batched skinny matmuls: one persistent launch computes a whole list of
  * independent y_g = x_g . What_g^T (same M for all, 1 <= M <= 16), e.g. every
  * projection of every layer of one decode step, which the pages' decode
