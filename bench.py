@@ -21,6 +21,8 @@ front.  Extra sections, each timed the same way, cover the rest of the path:
   verify_down            K = 17408, N = 5120, M = 1..16 (speculative verify)
   decode_step_64L        64 layers x {qkv, out, gate, up, down}: M = 5 as a
                          320-launch graph, and M = 1, 4, 5 as one persistent launch
+  attn_decode_256k       the K/V reads of a step's 16 attention layers at a 262,144-token
+                         4-bit cache, M = 1..5
   a8w4_prefill           M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
   a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048
 plus `roofline` for the dominant kernel and `cpu_baseline` (the oracle).
@@ -230,6 +232,46 @@ def bench_decode_step(torch, q4w, synthetic, reps, ms=(5, 1, 4)):
     return out
 
 
+def bench_attn(torch, q4w, synthetic, reps, t=262144, layers=16, ms=(1, 2, 3, 4, 5)):
+    """The K/V attention read of one decode step: the 16 full-attention
+    layers, each with its own 4-bit cache of t tokens (K and V rows of
+    H_kv * D = 4 x 256), read back to back at M = 1..5 query tokens (20
+    query heads).  Bytes per layer = both caches (codes and scales) + q + o."""
+    hq, hkv, d = 20, 4, 256
+    caches = []
+    for layer in range(layers):
+        kv = []
+        for which in range(2):
+            w = synthetic.weights_device(t, hkv * d, 50_000 + 2 * layer + which, std=1.0)
+            kv.extend(q4w.pack(w))
+            del w
+        caches.append(kv)
+    torch.cuda.synchronize()
+    cache_bytes = 2 * int(t * hkv * d * BYTES_PER_WEIGHT)
+    per_m = {}
+    for m in ms:
+        q = synthetic.activations_device(m * hq, d, 60_000 + m).reshape(m, hq, d)
+        outs = [torch.empty_like(q) for _ in range(layers)]
+        ws = torch.empty(max(q4w.attn_decode_ws_bytes(m, hq, hkv, d, t), 1), dtype=torch.uint8, device="cuda")
+
+        def step():
+            for (kc, ks, vc, vs), o in zip(caches, outs):
+                q4w.attn_decode(q, kc, ks, vc, vs, hkv, out=o, ws=ws)
+
+        if m == ms[0]:
+            warm_clocks(torch, step)
+        step()
+        dt = time_region(torch, lambda: [step() for _ in range(reps)], preroll=step) / reps
+        b = layers * (cache_bytes + 4 * m * hq * d)
+        per_m[str(m)] = dict(ms_16_layers=dt * 1e3, us_per_layer=dt / layers * 1e6, gbs=b / dt / 1e9,
+                             frac_of_peak=b / dt / 1e9 / HBM_PEAK_GBS)
+        del outs, ws
+    del caches
+    torch.cuda.empty_cache()
+    return dict(T=t, layers=layers, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                cache_bytes_per_layer=cache_bytes, per_M=per_m)
+
+
 def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
     """64 layers x 5 projections on the A8 route at M = 512, 1024 and 2048
     tokens (one packed weight set): per layer three activation quantizations
@@ -402,10 +444,10 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sections", default="decode,verify,step,prefill,pass",
+    ap.add_argument("--sections", default="decode,verify,step,attn,prefill,pass",
                     help="comma list of extra sections (decode is always run)")
     ap.add_argument("--only", default=None,
-                    help="run only this section (decode, verify, step, prefill, pass) and print its "
+                    help="run only this section (decode, verify, step, attn, prefill, pass) and print its "
                          "result; for profiling one kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
@@ -439,6 +481,7 @@ def main():
               "verify": lambda: bench_verify(torch, q4w, synthetic, max(args.steps // 3, 50), args.warmup),
               "step": lambda: bench_decode_step(torch, q4w, synthetic, reps=10),
               "prefill": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5)),
+              "attn": lambda: bench_attn(torch, q4w, synthetic, reps=max(args.steps // 10, 3)),
               "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
@@ -456,6 +499,10 @@ def main():
         log("[bench] decode_step_64L:",
             {mm: round(v["ms_batched"], 3) for mm, v in extra["decode_step_64L"].items()},
             f"ms batched; M=5 graph {extra['decode_step_64L']['5']['ms_graph']:.3f} ms")
+    if "attn" in sections:
+        extra["attn_decode_256k"] = bench_attn(torch, q4w, synthetic, reps=5)
+        log("[bench] attn_decode_256k:", {mm: round(v["gbs"]) for mm, v in extra["attn_decode_256k"]["per_M"].items()},
+            "GB/s")
     if "prefill" in sections:
         extra["a8w4_prefill"] = bench_prefill(torch, q4w, synthetic, reps=20)
         p = extra["a8w4_prefill"]

@@ -45,6 +45,7 @@ constexpr float kNegBig = -1.0e30f;       // running-max start (finite: no inf -
 constexpr float kRescaleGap = 8.0f;       // base-2 growth of the max that forces a rescale
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kMergeBatch = 16;           // slice loads in flight per thread in the merge
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -137,9 +138,11 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   const uint32_t lane_codes = (uint32_t)(g * (kD / 2) + 64 * hh);      // + key * row_codes
   const uint32_t lane_scales = (uint32_t)((g * (kD / kBlock) + 4 * hh) * 2);
 
-  uint4 kc[4], vc[4];         // this lane's 64 code bytes of K and of V
-  v2u ksc, vsc;               // its 4 block scales of K and of V (fp16 x 4)
-  auto load_k = [&](int tile) {
+  // this lane's 64 code bytes and 4 block scales (fp16 x 4) of K, two tiles'
+  // worth (the next tile's are requested before this one is used), and of V
+  uint4 kc[2][4], vc[4];
+  v2u ksc[2], vsc;
+  auto load_k = [&](int tile, uint4 (&kc)[4], v2u& ksc) {
     const int key = tile * kTileKeys + r;
     const bool live = tile < tile1 && key < T;
     const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
@@ -193,13 +196,9 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   const int slot = 8 * (dl >> 3) + (((dl & 3) << 1) | ((dl >> 2) & 1));
   const unsigned char* vread = vt + (8 * hh) * kVRow + 2 * slot;
 
-  int tile = tile0 + wave;
-  if (tile < tile1) {
-    load_k(tile);
-    load_v(tile);
-  }
-#pragma unroll 1
-  for (; tile < tile1; tile += kWaves) {
+  // one tile; kcur holds its K, the next tile's K goes into knext
+  auto process = [&](int tile, const uint4 (&kcur)[4], const v2u& kscur, uint4 (&knext)[4], v2u& ksnext) {
+    load_k(tile + kWaves, knext, ksnext);         // next tile of this wave (past the end: zeros)
     const int t0 = tile * kTileKeys;
     // ---- V: dequantize this lane's half row into the wave's LDS tile ------
 #pragma unroll
@@ -213,11 +212,10 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     f16v s = {};
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const uint4 a = dequant8(word(kc, c), scale2(ksc, c >> 2));
+      const uint4 a = dequant8(word(kcur, c), scale2(kscur, c >> 2));
       const uint4 b = lds.qt[c * 64 + lane];
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), s, 0, 0, 0);
     }
-    load_k(tile + kWaves);
 
     // ---- softmax (base 2), lazy running max -------------------------------
     float sv[16];
@@ -276,6 +274,17 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, as_h8(bb), o[dt], 0, 0, 0);
       }
     }
+  };
+
+  int tile = tile0 + wave;
+  if (tile < tile1) {
+    load_k(tile, kc[0], ksc[0]);
+    load_v(tile);
+  }
+#pragma unroll 1
+  for (; tile < tile1; tile += 2 * kWaves) {
+    process(tile, kc[0], ksc[0], kc[1], ksc[1]);
+    if (tile + kWaves < tile1) process(tile + kWaves, kc[1], ksc[1], kc[0], ksc[0]);
   }
   l_run += __shfl_xor(l_run, 32, 64);
 
@@ -341,26 +350,62 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 }
 
 // ---- kernel 2: merge the slices -------------------------------------------
-// grid (H_kv * R), one thread per channel.
-__global__ void __launch_bounds__(kD)
+// grid (H_kv * R, D / 64), 256 threads: thread (ss, dd) takes channel
+// 64 blockIdx.y + dd of slices ss, ss + 4, ...; the four parts are summed in
+// a fixed order.
+constexpr int kMergeParts = 4;
+__global__ void __launch_bounds__(256)
 attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                   uint16_t* __restrict__ out, int M, int Hq, int Hkv, int S) {
+  __shared__ float acc_s[kMergeParts][64], l_s[kMergeParts][64];
   const int G = Hq / Hkv;
   const int R = M * G;
   const int g = blockIdx.x / R;
   const int r = blockIdx.x - g * R;
-  const int d = threadIdx.x;
+  const int ss = threadIdx.x >> 6, dd = threadIdx.x & 63;
+  const int d = 64 * blockIdx.y + dd;
+  const size_t stride = (size_t)Hkv * R;          // rows between consecutive slices
+  const float* ml = part_ml + 2 * ((size_t)g * R + r);
+  const float* po = part_o + ((size_t)g * R + r) * kD + d;
   float mmax = kNegBig;
-  for (int s = 0; s < S; ++s) mmax = fmaxf(mmax, part_ml[2 * (((size_t)s * Hkv + g) * R + r)]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const size_t row = ((size_t)s * Hkv + g) * R + r;
-    const float w = __builtin_amdgcn_exp2f(part_ml[2 * row] - mmax);
-    l += part_ml[2 * row + 1] * w;
-    acc += part_o[row * kD + d] * w;
+  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+    float mv[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) mv[i] = ml[2 * min(s0 + i, S - 1) * stride];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) mmax = fmaxf(mmax, mv[i]);
   }
-  const int m = r / G, hq = g * G + r % G;
-  out[((size_t)m * Hq + hq) * kD + d] = __half_as_ushort(__float2half_rn(acc / l));
+  float l = 0.f, acc = 0.f;
+  for (int s0 = ss; s0 < S; s0 += kMergeParts * kMergeBatch) {
+    float ov[kMergeBatch], mv[kMergeBatch], lv[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int s = min(s0 + kMergeParts * i, S - 1);
+      ov[i] = po[(size_t)s * stride * kD];
+      mv[i] = ml[2 * s * stride];
+      lv[i] = ml[2 * s * stride + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + kMergeParts * i < S) {
+        const float w = __builtin_amdgcn_exp2f(mv[i] - mmax);
+        l += lv[i] * w;
+        acc += ov[i] * w;
+      }
+  }
+  acc_s[ss][dd] = acc;
+  l_s[ss][dd] = l;
+  __syncthreads();
+  if (ss == 0) {
+    float a = 0.f, lt = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergeParts; ++i) {
+      a += acc_s[i][dd];
+      lt += l_s[i][dd];
+    }
+    const int m = r / G, hq = g * G + r % G;
+    out[((size_t)m * Hq + hq) * kD + d] = __half_as_ushort(__float2half_rn(a / lt));
+  }
 }
 
 }  // namespace
@@ -397,8 +442,8 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const u
                      v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(Hkv * M * (Hq / Hkv)), dim3(kD), 0, s, part_o, part_ml, out, M,
-                     Hq, Hkv, S);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(Hkv * M * (Hq / Hkv), kD / 64), dim3(256), 0, s, part_o, part_ml,
+                     out, M, Hq, Hkv, S);
   return hipGetLastError();
 }
 
