@@ -24,9 +24,12 @@
 //  * Softmax in base 2, in fp32, with a lazy running max: the output is
 //    rescaled only when some row's max grows by more than 8 (p <= 256).
 //  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  Each lane dequantizes its
-//    key's V half-row into a wave-private LDS tile; the product reads that
-//    tile transposed (8 keys of one channel per lane); P^T comes from the
-//    scores' registers through two v_permlane32_swap per 16 keys.
+//    key's V half-row into a wave-private LDS tile (512-byte rows, 16-byte
+//    chunks XOR-swizzled by key so that neither the row writes nor the
+//    column reads meet bank conflicts); the product's V^T operand comes out
+//    of that tile with the transposing LDS read (ds_read_b64_tr_b16: four
+//    keys of one channel per lane per read); P^T comes from the scores'
+//    registers through two v_permlane32_swap per 16 keys.
 //  * The 8 waves' partial results are combined in LDS, each workgroup writes
 //    one partial (rows < R only), and a second kernel merges the slices.
 
@@ -40,7 +43,9 @@ constexpr int kD = kAttnHeadDim;          // head dimension (256)
 constexpr int kTileKeys = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVRow = 528;                // bytes per dequantized V row in LDS (512 + pad)
+constexpr int kVRow = 512;                // bytes per dequantized V row in LDS
+constexpr int kVTile = kTileKeys * kVRow; // bytes per wave's V tile
+constexpr int kQtBytes = 16 * 64 * 16;    // Q^T operands in LDS
 constexpr float kNegBig = -1.0e30f;       // running-max start (finite: no inf - inf)
 constexpr float kRescaleGap = 8.0f;       // base-2 growth of the max that forces a rescale
 constexpr int kRsrcWord3 = 0x00020000;
@@ -53,10 +58,12 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-struct AttnLds {
-  uint4 qt[16 * 64];                          // Q^T B operands: [product c][lane]
-  unsigned char v[kWaves][kTileKeys * kVRow]; // per-wave dequantized V tile, [key][slot]
-};
+// LDS: Q^T B operands [product c][lane] (uint4), then one dequantized V tile
+// per wave, [key][512 bytes].  After the key loop the whole area serves the
+// combine of the 8 waves.
+constexpr int kLdsBytes = kQtBytes + kWaves * kVTile;
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -78,6 +85,12 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, h2 d2) {
 
 __device__ __forceinline__ h8 as_h8(uint4 v) { return __builtin_bit_cast(h8, v); }
 
+// max of x over lanes l and l ^ 32
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // lanes 32..63 of a <-> lanes 0..31 of b
 __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
@@ -93,7 +106,8 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
                     const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
                     const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
                     float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
-  __shared__ AttnLds lds;
+  __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  uint4* qt = reinterpret_cast<uint4*>(lds);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -120,7 +134,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       o.z = (w.y & 0xFFFFu) | (w.w << 16);          // (e2, e6)
       o.w = (w.y >> 16) | (w.w & 0xFFFF0000u);      // (e3, e7)
     }
-    lds.qt[e] = o;
+    qt[e] = o;
   }
   __syncthreads();
 
@@ -140,6 +154,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
   // this lane's 64 code bytes and 4 block scales (fp16 x 4) of K, two tiles'
   // worth (the next tile's are requested before this one is used), and of V
+  // (the next tile's are requested as soon as this one sits in LDS)
   uint4 kc[2][4], vc[4];
   v2u ksc[2], vsc;
   auto load_k = [&](int tile, uint4 (&kc)[4], v2u& ksc) {
@@ -188,34 +203,84 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
 
-  unsigned char* vt = lds.v[wave];
-  // V tile transposed read: lane (d, hh) takes channel d = 32 dt + (lane & 31)
-  // of keys 16 c' + 8 hh + j; the channel's slot inside its group of 8 is
-  // (0, 2, 4, 6, 1, 3, 5, 7)[d % 8] (the dequantized pair order).
-  const int dl = lane & 31;
-  const int slot = 8 * (dl >> 3) + (((dl & 3) << 1) | ((dl >> 2) & 1));
-  const unsigned char* vread = vt + (8 * hh) * kVRow + 2 * slot;
+  // ---- the wave's V tile: key t's row holds its 256 channels as fp16 in
+  // the dequantized pair order (column 8 i + (0, 2, 4, 6, 1, 3, 5, 7)[e] is
+  // channel 8 i + e); 16-byte chunk n of row t sits at chunk n ^ sw(t),
+  // sw(t) = 4 (t % 4) + (t / 4) % 4.
+  const int vt = kQtBytes + wave * kVTile;
+  // row writes: lane (key r, half hh) writes chunk 16 hh + c at wr ^ 16 c
+  const int wr = vt + r * kVRow + 256 * hh + 16 * (4 * (r & 3) + ((r >> 2) & 3));
+  // transposed reads (A operand of the 32 x 32 x 16 product): lane l takes
+  // column 32 dt + l % 32 of keys 16 cp + 8 (l / 32) + 4 j + (0..3).  Within
+  // each 16-lane group, lane 4 k + i / 4 reads the 8 bytes that the
+  // transpose hands to lane i as its element k: key 4 j + ((l >> 2) & 3),
+  // columns 4 (l & 3) + (0..3) of the group's 16.  The address for dt % 4 = e
+  // is rd[j] + 64 (e ^ x); cp and dt / 4 only add constants (8192 cp + 256 (dt / 4)).
+  const int x64 = 64 * ((lane >> 2) & 3);
+  int rd[2];
+  {
+    const int grp = (lane >> 4) & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = (2 * (lane >> 5) + j) & 3;
+      rd[j] = vt + (8 * (lane >> 5) + 4 * j) * kVRow + x64 * (kVRow / 64) +
+              16 * ((2 * grp + ((lane & 3) >> 1)) ^ u) + 8 * (lane & 1);
+    }
+  }
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  lds_u8* const lds3 = (lds_u8*)lds;
 
-  // one tile; kcur holds its K, the next tile's K goes into knext
+  // one tile; kcur holds its K, the next tile's K goes into knext.  The
+  // scheduling fences keep each LDS operand read three products ahead of its
+  // use (the compiler would otherwise issue it just before the product).
   auto process = [&](int tile, const uint4 (&kcur)[4], const v2u& kscur, uint4 (&knext)[4], v2u& ksnext) {
     load_k(tile + kWaves, knext, ksnext);         // next tile of this wave (past the end: zeros)
     const int t0 = tile * kTileKeys;
     // ---- V: dequantize this lane's half row into the wave's LDS tile ------
+    int w = wr;
+    asm volatile("" : "+v"(w));                   // addresses made per tile, not held in registers
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       const uint4 p = dequant8(word(vc, c), scale2(vsc, c >> 2));
-      *reinterpret_cast<uint4*>(vt + r * kVRow + 256 * hh + 16 * c) = p;
+      *reinterpret_cast<uint4*>(lds + (w ^ (16 * c))) = p;
     }
     load_v(tile + kWaves);                        // next tile of this wave (past the end: zeros)
 
     // ---- scores S^T[t, r] ---------------------------------------------------
     f16v s = {};
+    uint4 bq[4];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) bq[c] = qt[c * 64 + lane];
+    uint4 a = dequant8(word(kcur, 0), scale2(kscur, 0));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const uint4 a = dequant8(word(kcur, c), scale2(kscur, c >> 2));
-      const uint4 b = lds.qt[c * 64 + lane];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(b), s, 0, 0, 0);
+      if (c + 3 < 16) bq[(c + 3) & 3] = qt[(c + 3) * 64 + lane];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(bq[c & 3]), s, 0, 0, 0);
+      if (c + 1 < 16) a = dequant8(word(kcur, c + 1), scale2(kscur, (c + 1) >> 2));
+      __builtin_amdgcn_sched_barrier(0);
     }
+
+    // ---- V^T operands of the first three value products (read ahead) ------
+    int ra[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int b = rd[j];
+      asm volatile("" : "+v"(b));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ra[j][e] = b + (x64 ^ (64 * e));
+    }
+    auto load_a = [&](int idx) {                  // product idx: cp = idx / 8, dt = idx % 8
+      const int dt = idx & 7;
+      const int off = 16 * kVRow * (idx >> 3) + 256 * (dt >> 2);
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + ra[0][dt & 3] + off));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + ra[1][dt & 3] + off));
+      return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    h8 av[4];
+#pragma unroll
+    for (int idx = 0; idx < 3; ++idx) av[idx] = load_a(idx);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- softmax (base 2), lazy running max -------------------------------
     float sv[16];
@@ -231,7 +296,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     float mx = sv[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleGap) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -260,19 +325,16 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     swap32(pk[1], pk[3]);
     swap32(pk[4], pk[6]);
     swap32(pk[5], pk[7]);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T[d, r] += V^T[d, t] P^T[t, r] ---------------------------------
 #pragma unroll
-    for (int cp = 0; cp < 2; ++cp) {
+    for (int idx = 0; idx < 16; ++idx) {
+      if (idx + 3 < 16) av[(idx + 3) & 3] = load_a(idx + 3);
+      const int cp = idx >> 3;
       const uint4 bb = make_uint4(pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        h8 a;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          a[j] = *reinterpret_cast<const _Float16*>(vread + (16 * cp + j) * kVRow + 64 * dt);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, as_h8(bb), o[dt], 0, 0, 0);
-      }
+      o[idx & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[idx & 3], as_h8(bb), o[idx & 7], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -290,7 +352,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
   // ---- combine the 8 waves in LDS (the V tiles are free now) ----------------
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&lds.v[0][0]);    // [wave][idx][lane] float4s + max
+  float* red = reinterpret_cast<float*>(lds);             // [wave][idx][lane] float4s + max
   float* mxs = red + 4 * 32 * 64 * 4;                     // after 4 waves' outputs: [wave][32]
   if (hh == 0) mxs[wave * 32 + r] = m_run;
   __syncthreads();
@@ -339,9 +401,11 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)     // d = 32 dt + 8 i + 4 hh + (0..3)
-        *reinterpret_cast<float4*>(po + 32 * dt + 8 * i + 4 * hh) =
-            make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
+      for (int i = 0; i < 4; ++i) {   // rows 8 i + 4 hh + (0..3): channels 8 i + (0, 4, 1, 5) + 2 hh
+        float* pd = po + 32 * dt + 8 * i + 2 * hh;
+        *reinterpret_cast<float2*>(pd) = make_float2(o[dt][4 * i], o[dt][4 * i + 2]);
+        *reinterpret_cast<float2*>(pd + 4) = make_float2(o[dt][4 * i + 1], o[dt][4 * i + 3]);
+      }
     if (hh == 0) {
       part_ml[2 * row] = m_all;
       part_ml[2 * row + 1] = l_run;
@@ -351,13 +415,14 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
 // ---- kernel 2: merge the slices -------------------------------------------
 // grid (H_kv * R, D / 64), 256 threads: thread (ss, dd) takes channel
-// 64 blockIdx.y + dd of slices ss, ss + 4, ...; the four parts are summed in
-// a fixed order.
+// 64 blockIdx.y + dd of slices ss, ss + 4, ... with its own running max (one
+// batch of loads in flight for up to 64 slices per part); the four parts are
+// then combined in a fixed order.
 constexpr int kMergeParts = 4;
 __global__ void __launch_bounds__(256)
 attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                   uint16_t* __restrict__ out, int M, int Hq, int Hkv, int S) {
-  __shared__ float acc_s[kMergeParts][64], l_s[kMergeParts][64];
+  __shared__ float m_s[kMergeParts][64], l_s[kMergeParts][64], a_s[kMergeParts][64];
   const int G = Hq / Hkv;
   const int R = M * G;
   const int g = blockIdx.x / R;
@@ -367,15 +432,7 @@ attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ pa
   const size_t stride = (size_t)Hkv * R;          // rows between consecutive slices
   const float* ml = part_ml + 2 * ((size_t)g * R + r);
   const float* po = part_o + ((size_t)g * R + r) * kD + d;
-  float mmax = kNegBig;
-  for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
-    float mv[kMergeBatch];
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) mv[i] = ml[2 * min(s0 + i, S - 1) * stride];
-#pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) mmax = fmaxf(mmax, mv[i]);
-  }
-  float l = 0.f, acc = 0.f;
+  float m = kNegBig, l = 0.f, acc = 0.f;
   for (int s0 = ss; s0 < S; s0 += kMergeParts * kMergeBatch) {
     float ov[kMergeBatch], mv[kMergeBatch], lv[kMergeBatch];
 #pragma unroll
@@ -385,26 +442,39 @@ attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ pa
       mv[i] = ml[2 * s * stride];
       lv[i] = ml[2 * s * stride + 1];
     }
+    float bm = m;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + kMergeParts * i < S) bm = fmaxf(bm, mv[i]);
+    const float sc = __builtin_amdgcn_exp2f(m - bm);
+    l *= sc;
+    acc *= sc;
+    m = bm;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i)
       if (s0 + kMergeParts * i < S) {
-        const float w = __builtin_amdgcn_exp2f(mv[i] - mmax);
+        const float w = __builtin_amdgcn_exp2f(mv[i] - m);
         l += lv[i] * w;
         acc += ov[i] * w;
       }
   }
-  acc_s[ss][dd] = acc;
+  m_s[ss][dd] = m;
   l_s[ss][dd] = l;
+  a_s[ss][dd] = acc;
   __syncthreads();
   if (ss == 0) {
+    float mt = m_s[0][dd];
+#pragma unroll
+    for (int i = 1; i < kMergeParts; ++i) mt = fmaxf(mt, m_s[i][dd]);
     float a = 0.f, lt = 0.f;
 #pragma unroll
     for (int i = 0; i < kMergeParts; ++i) {
-      a += acc_s[i][dd];
-      lt += l_s[i][dd];
+      const float w = __builtin_amdgcn_exp2f(m_s[i][dd] - mt);
+      a += a_s[i][dd] * w;
+      lt += l_s[i][dd] * w;
     }
-    const int m = r / G, hq = g * G + r % G;
-    out[((size_t)m * Hq + hq) * kD + d] = __half_as_ushort(__float2half_rn(a / lt));
+    const int mq = r / G, hq = g * G + r % G;
+    out[((size_t)mq * Hq + hq) * kD + d] = __half_as_ushort(__float2half_rn(a / lt));
   }
 }
 
