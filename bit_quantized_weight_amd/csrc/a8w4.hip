@@ -25,7 +25,8 @@
 //    so a wave copies each 32 x 32 operand (1 KB) from the workspace straight
 //    into LDS with one buffer load that writes LDS; weight codes are unpacked
 //    into LDS with an XOR swizzle (conflict-free 128-bit reads), and each
-//    column's two block scales and the magic offset sit in one 16-byte entry.
+//    column's two block scales sit in one 8-byte entry (the magic offset term
+//    is formed from them when they are read).
 
 #include "q4w_internal.h"
 #include <hip/hip_fp16.h>
