@@ -99,7 +99,10 @@ __device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
 }
 
 // ---- kernel 1: one partial result per (K/V head, key slice) ---------------
-// grid (S, H_kv), 8 waves.  Slice s covers key tiles [s * tps, (s + 1) * tps).
+// grid (S, H_kv), 8 waves.  Slice s covers the key tiles s + k S, k < tps:
+// the slices interleave, so at any time all workgroups read neighbouring
+// tiles (the whole chip sweeps the cache as one window, which streams faster
+// than S separate regions).
 // part_o: [S][H_kv][R][D] fp32, part_ml: [S][H_kv][R][2] (base-2 max, sum).
 __global__ void __launch_bounds__(kThreads)
 attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
@@ -118,8 +121,10 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   const int G = Hq / Hkv;
   const int R = M * G;
   const int ntiles = (T + kTileKeys - 1) / kTileKeys;
-  const int tile0 = split * tps;
-  const int tile1 = min(ntiles, tile0 + tps);
+  const int S = gridDim.x;
+  // physical tile of this slice's k-th tile, and whether it exists
+  auto phys = [&](int k) { return k * S + split; };
+  auto exists = [&](int k) { return k < tps && phys(k) < ntiles; };
 
   // ---- Q^T into LDS: entry (c, lane') holds Q[r', 128 h' + 8 c + (0,4,1,5,2,6,3,7)]
   for (int e = tid; e < 16 * 64; e += kThreads) {
@@ -157,9 +162,9 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   // (the next tile's are requested as soon as this one sits in LDS)
   uint4 kc[2][4], vc[4];
   v2u ksc[2], vsc;
-  auto load_k = [&](int tile, uint4 (&kc)[4], v2u& ksc) {
-    const int key = tile * kTileKeys + r;
-    const bool live = tile < tile1 && key < T;
+  auto load_k = [&](int k, uint4 (&kc)[4], v2u& ksc) {
+    const int key = phys(k) * kTileKeys + r;
+    const bool live = exists(k) && key < T;
     const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
     const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
 #pragma unroll
@@ -169,9 +174,9 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
     ksc = __builtin_amdgcn_raw_buffer_load_b64(rks, os, 0, 0);
   };
-  auto load_v = [&](int tile) {
-    const int key = tile * kTileKeys + r;
-    const bool live = tile < tile1 && key < T;
+  auto load_v = [&](int k) {
+    const int key = phys(k) * kTileKeys + r;
+    const bool live = exists(k) && key < T;
     const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
     const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
 #pragma unroll
@@ -233,9 +238,9 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   // one tile; kcur holds its K, the next tile's K goes into knext.  The
   // scheduling fences keep each LDS operand read three products ahead of its
   // use (the compiler would otherwise issue it just before the product).
-  auto process = [&](int tile, const uint4 (&kcur)[4], const v2u& kscur, uint4 (&knext)[4], v2u& ksnext) {
-    load_k(tile + kWaves, knext, ksnext);         // next tile of this wave (past the end: zeros)
-    const int t0 = tile * kTileKeys;
+  auto process = [&](int k, const uint4 (&kcur)[4], const v2u& kscur, uint4 (&knext)[4], v2u& ksnext) {
+    load_k(k + kWaves, knext, ksnext);            // next tile of this wave (past the end: zeros)
+    const int t0 = phys(k) * kTileKeys;
     // ---- V: dequantize this lane's half row into the wave's LDS tile ------
     int w = wr;
     asm volatile("" : "+v"(w));                   // addresses made per tile, not held in registers
@@ -244,7 +249,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       const uint4 p = dequant8(word(vc, c), scale2(vsc, c >> 2));
       *reinterpret_cast<uint4*>(lds + (w ^ (16 * c))) = p;
     }
-    load_v(tile + kWaves);                        // next tile of this wave (past the end: zeros)
+    load_v(k + kWaves);                           // next tile of this wave (past the end: zeros)
 
     // ---- scores S^T[t, r] ---------------------------------------------------
     f16v s = {};
@@ -338,15 +343,15 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     }
   };
 
-  int tile = tile0 + wave;
-  if (tile < tile1) {
-    load_k(tile, kc[0], ksc[0]);
-    load_v(tile);
+  int k = wave;                                 // this wave's tiles: k, k + 8, ... of the slice
+  if (exists(k)) {
+    load_k(k, kc[0], ksc[0]);
+    load_v(k);
   }
 #pragma unroll 1
-  for (; tile < tile1; tile += 2 * kWaves) {
-    process(tile, kc[0], ksc[0], kc[1], ksc[1]);
-    if (tile + kWaves < tile1) process(tile + kWaves, kc[1], ksc[1], kc[0], ksc[0]);
+  for (; exists(k); k += 2 * kWaves) {
+    process(k, kc[0], ksc[0], kc[1], ksc[1]);
+    if (exists(k + kWaves)) process(k + kWaves, kc[1], ksc[1], kc[0], ksc[0]);
   }
   l_run += __shfl_xor(l_run, 32, 64);
 
