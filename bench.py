@@ -25,6 +25,8 @@ front.  Extra sections, each timed the same way, cover the rest of the path:
                          4-bit cache, M = 1..5
   a8w4_prefill           M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
   a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048
+  read_ceiling           a plain streaming read (q4w_stream_read) of the same byte
+                         counts: what this GPU reaches, beside the 8 TB/s peak
 plus `roofline` for the dominant kernel and `cpu_baseline` (the oracle).
 """
 
@@ -272,6 +274,45 @@ def bench_attn(torch, q4w, synthetic, reps, t=262144, layers=16, ms=(1, 2, 3, 4,
                 cache_bytes_per_layer=cache_bytes, per_M=per_m)
 
 
+def bench_ceiling(torch, q4w, reps=40):
+    """What a plain streaming read (q4w_stream_read) reaches on this GPU for
+    the byte counts of the HBM-bound workloads: one decode_gate_up launch
+    (50.2 MB), one attention layer (302 MB) and a long stream (2.4 GB), each
+    rotating over copies in a 2.4 GB buffer so nothing is served from the
+    256 MB Infinity Cache.  The achievable ceiling beside the 8 TB/s peak."""
+    total = 2_415_919_104
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    cases = {"one_launch_50MB": (50_180_096, 200), "attn_layer_302MB": (301_989_888, reps),
+             "long_stream_2400MB": (total, 5)}
+    shapes = [(256, 512), (1024, 256), (2048, 256)]
+    res = {}
+    for name, (nbytes, n) in cases.items():
+        stride = (nbytes + 255) // 256 * 256
+        views = [buf[i * stride:i * stride + nbytes] for i in range(max(1, total // stride))]
+        best = None
+        per_shape = {}
+        for grid, block in shapes:
+            out = torch.empty(grid, dtype=torch.int32, device="cuda")
+
+            def run():
+                for i in range(n):
+                    q4w.stream_read(views[i % len(views)], grid, block, out)
+
+            if best is None:
+                warm_clocks(torch, run)
+            dt = time_region(torch, run, preroll=run) / n
+            per_shape[f"{grid}x{block}"] = dict(us_per_launch=dt * 1e6, gbs=nbytes / dt / 1e9)
+            if best is None or dt < best[0]:
+                best = (dt, f"{grid}x{block}")
+        res[name] = dict(bytes=nbytes, copies=len(views), best_shape=best[1], us_per_launch=best[0] * 1e6,
+                         gbs=nbytes / best[0] / 1e9, frac_of_peak=nbytes / best[0] / 1e9 / HBM_PEAK_GBS,
+                         per_shape=per_shape)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
     """64 layers x 5 projections on the A8 route at M = 512, 1024 and 2048
     tokens (one packed weight set): per layer three activation quantizations
@@ -444,10 +485,10 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sections", default="decode,verify,step,attn,prefill,pass",
+    ap.add_argument("--sections", default="decode,verify,step,attn,prefill,pass,ceiling",
                     help="comma list of extra sections (decode is always run)")
     ap.add_argument("--only", default=None,
-                    help="run only this section (decode, verify, step, attn, prefill, pass) and print its "
+                    help="run only this section (decode, verify, step, attn, prefill, pass, ceiling) and print its "
                          "result; for profiling one kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
@@ -482,7 +523,8 @@ def main():
               "step": lambda: bench_decode_step(torch, q4w, synthetic, reps=10),
               "prefill": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5)),
               "attn": lambda: bench_attn(torch, q4w, synthetic, reps=max(args.steps // 10, 3)),
-              "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3)}[args.only]
+              "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3),
+              "ceiling": lambda: bench_ceiling(torch, q4w)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
 
@@ -508,6 +550,9 @@ def main():
         p = extra["a8w4_prefill"]
         log(f"[bench] a8w4_prefill: GEMM {p['ms_gemm']:.3f} ms, route {p['ms_route']:.3f} ms, "
             f"act quant {p['ms_act_quant']:.4f} ms")
+    if "ceiling" in sections:
+        extra["read_ceiling"] = bench_ceiling(torch, q4w)
+        log("[bench] read_ceiling:", {k_: round(v_["gbs"]) for k_, v_ in extra["read_ceiling"].items()}, "GB/s")
     if "pass" in sections:
         extra["a8w4_prefill_pass_64L"] = bench_prefill_pass(torch, q4w, synthetic, reps=3)
         for m_, r_ in extra["a8w4_prefill_pass_64L"]["per_M"].items():

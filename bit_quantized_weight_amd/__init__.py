@@ -1,4 +1,5 @@
-"""MI355X-native 4-bit block-quantized weight matmul (decode and A8 prefill).
+"""MI355X-native 4-bit block-quantized weight matmul (decode and A8 prefill)
+and the decode-time read of a 4-bit K/V cache.
 
 The compute lives in the HIP library ``libq4w.so`` (hand-written gfx950
 kernels behind a C ABI declared in ``include/q4w.h``); this package is only
@@ -27,4 +28,5 @@ from .binding import (  # noqa: F401
     lib_path,
     pack,
     q4_gemv_skinny_raw,
+    stream_read,
 )

@@ -88,6 +88,8 @@ def lib():
     L.q4_gemv_batched_plan.restype = i32
     L.q4_gemv_batched_run.argtypes = [ctypes.POINTER(BatchedPlan), vp]
     L.q4_gemv_batched_run.restype = i32
+    L.q4w_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
+    L.q4w_stream_read.restype = i32
     L.q4w_status_str.argtypes = [i32]
     L.q4w_status_str.restype = ctypes.c_char_p
     L.q4w_last_hip_error.argtypes = []
@@ -352,3 +354,19 @@ def batched_plan(items):
     _check("q4_gemv_batched_plan", lib().q4_gemv_batched_plan(m, descs, len(items), _ptr(ws), nb,
                                                               ctypes.byref(plan)))
     return Batch(plan, ws, [t for it in items for t in it])
+
+
+def stream_read(buf, grid=256, block=512, out=None):
+    """Plain streaming read of a device tensor's bytes (a measurement helper):
+    returns out, int32 [grid], each workgroup's XOR of the words it read."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    if out is None:
+        out = torch.empty(grid, dtype=torch.int32, device=buf.device)
+    _need(out, torch.int32, "out")
+    _need_shape(out, (grid,), "out")
+    nbytes = buf.numel() * buf.element_size()
+    _check("q4w_stream_read", lib().q4w_stream_read(_ptr(buf), nbytes, _ptr(out), grid, block, _stream()))
+    return out
+

@@ -280,6 +280,14 @@ int q4_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_
                                             n_kv_heads, T, ws, stream));
 }
 
+int q4w_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, int block, hipStream_t stream) {
+  if (!out || (!buf && bytes > 0)) return Q4W_ERR_INVALID_ARG;
+  if (grid < 1 || grid > 65536 || block < 64 || block > 1024 || block % 64 != 0) return Q4W_ERR_INVALID_ARG;
+  if (bytes % 16 != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return Q4W_ERR_MISALIGNED;
+  return hip_status(q4w::launch_stream_read(buf, bytes, out, grid, block, stream));
+}
+
 const char* q4w_status_str(int status) {
   switch (status) {
     case Q4W_OK: return "OK";

@@ -103,6 +103,9 @@ constexpr int kAttnHeadDim = 256;   // head dimension the kernel is built for
 constexpr int kAttnMaxRows = 32;    // M * (H_q / H_kv): query rows of one K/V head
 int attn_splits(int M, int Hq, int Hkv, int64_t T);
 size_t attn_ws_bytes(int M, int Hq, int Hkv, int64_t T);
+// plain streaming read of a device buffer (measurement helper); out[grid]
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, int block,
+                              hipStream_t s);
 hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const uint16_t* k_scales,
                               const uint8_t* v_codes, const uint16_t* v_scales, uint16_t* out, int M,
                               int Hq, int Hkv, int64_t T, void* ws, hipStream_t s);

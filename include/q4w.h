@@ -1,7 +1,7 @@
 /*
  * q4w.h -- C ABI of the MI355X (gfx950) 4-bit block-quantized weight matmul.
  *
- * Three operations, each from the pages on 4-bit LLM inference:
+ * Four operations, each from the pages on 4-bit LLM inference:
  *
  *   q4_pack            weight quantization into the 4-bit block format.
  *                      "Qwen3.8-27B at 256K on a 24GB RTX PRO 4000 SFF"
@@ -16,6 +16,9 @@
  *                      matrix-core contraction.  "Qwen3.8-27B on RTX 4090:
  *                      5,000 tok/s Prefill Reproduced" (page 5), section
  *                      "Why the A8 artifact matters".
+ *   q4_attn_decode     the decode-time read of a K/V cache held in the same
+ *                      4-bit format.  Page 3, the architecture and bandwidth
+ *                      paragraphs (16 full-attention layers with Q4 K and V).
  *
  * Format (the pages name it but do not define it; this is the reading used):
  *   W is [N, K] fp32, row n = output n, K = reduction width.  Y = X . What^T.
@@ -285,6 +288,22 @@ size_t q4_gemv_batched_ws_bytes(int M, const q4w_gemv_desc* descs, int count);
 int q4_gemv_batched_plan(int M, const q4w_gemv_desc* descs, int count, void* ws,
                          size_t ws_bytes, q4w_batched_plan* plan);
 int q4_gemv_batched_run(const q4w_batched_plan* plan, hipStream_t stream);
+
+/*
+ * q4w_stream_read: a measurement helper, not a step of the method.  A plain
+ *   streaming read of `bytes` bytes at `buf` by `grid` workgroups of `block`
+ *   threads, each thread keeping four 16-byte loads in flight, grid-stride
+ *   (the whole chip reads one narrow window of the buffer at a time).  It
+ *   gives the read rate this GPU reaches for a given launch shape, the
+ *   achievable ceiling that the HBM-bound kernels above are measured against
+ *   (next to the published 8 TB/s peak).  out[w] (uint32, `grid` entries) is
+ *   the XOR of the 32-bit words that workgroup w read, a checksum: the XOR of
+ *   out[0 .. grid) is the XOR of every word of the buffer.
+ *   buf 16-byte aligned (may be NULL when bytes == 0), bytes % 16 == 0 (else
+ *   UNSUPPORTED_SHAPE), out 4-byte aligned, 1 <= grid <= 65536,
+ *   64 <= block <= 1024 with block % 64 == 0 (else INVALID_ARG).
+ */
+int q4w_stream_read(const void* buf, size_t bytes, uint32_t* out, int grid, int block, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* q4w_status_str(int status);

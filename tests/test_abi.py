@@ -305,3 +305,45 @@ def test_batched_checks(L):
     run = L.q4_gemv_batched_run
     assert run(None, NUL) == INVALID
     assert run(ctypes.byref(binding.BatchedPlan()), NUL) == INVALID  # never planned
+
+
+def test_attn_checks(L):
+    """q4_attn_decode: shape, pointer, alignment and workspace checks, and the
+    workspace size (S key slices x H_kv x R rows of D fp32 partials, then the
+    per-row max and sum)."""
+    ws = L.q4_attn_decode_ws_bytes
+    # T = 262144, M = 5, 20 query heads over 4 K/V heads: 64 slices x 4 x 25 rows
+    assert ws(5, 20, 4, 256, 262144) == 64 * 4 * 25 * 256 * 4 + 64 * 4 * 25 * 2 * 4
+    # T = 100: 4 tiles of 32 keys -> one slice
+    assert ws(1, 20, 4, 256, 100) == 4 * 5 * 256 * 4 + 4 * 5 * 2 * 4
+    assert ws(0, 20, 4, 256, 100) == 0 and ws(1, 20, 4, 128, 100) == 0 and ws(1, 20, 3, 256, 100) == 0
+    assert ws(5, 40, 4, 256, 100) == 0           # R = 50 > 32
+    assert ws(5, 20, 4, 256, 4) == 0             # T < M
+    assert ws(1, 4, 4, 256, (1 << 22) - 1) > 0 and ws(1, 4, 4, 256, 1 << 22) == 0   # 32-bit cache offsets
+    need = ws(5, 20, 4, 256, 1000)
+    f = L.q4_attn_decode
+    args = lambda **kw: [p(kw.get("q", A)), p(kw.get("kc", A)), p(kw.get("ks", A)), p(kw.get("vc", A)),
+                         p(kw.get("vs", A)), p(kw.get("o", A)), kw.get("m", 5), kw.get("hq", 20), 4, 256,
+                         kw.get("t", 1000), p(kw.get("ws", A)), kw.get("wsb", need), NUL]
+    assert f(*args(m=0)) == INVALID
+    assert f(*args(t=-1)) == INVALID
+    assert f(*args(hq=21)) == SHAPE
+    assert f(*args(t=4)) == SHAPE
+    assert f(*args(q=0)) == INVALID and f(*args(vs=0)) == INVALID and f(*args(o=0)) == INVALID
+    assert f(*args(q=U)) == ALIGN and f(*args(kc=A + 8)) == ALIGN and f(*args(vc=A + 8)) == ALIGN
+    assert f(*args(ks=A + 4)) == ALIGN and f(*args(vs=A + 4)) == ALIGN and f(*args(o=A + 1)) == ALIGN
+    assert f(*args(ws=0)) == WS and f(*args(wsb=need - 1)) == WS
+    assert f(*args(ws=A + 16)) == ALIGN
+
+
+def test_stream_read_checks(L):
+    f = L.q4w_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(p(A), 1024, NUL, 256, 512, NUL) == INVALID
+    assert f(NUL, 1024, p(A), 256, 512, NUL) == INVALID
+    assert f(p(A), 1024, p(A), 0, 512, NUL) == INVALID and f(p(A), 1024, p(A), 65537, 512, NUL) == INVALID
+    assert f(p(A), 1024, p(A), 256, 32, NUL) == INVALID and f(p(A), 1024, p(A), 256, 96 + 16, NUL) == INVALID
+    assert f(p(A), 1024, p(A), 256, 2048, NUL) == INVALID
+    assert f(p(A), 1000, p(A), 256, 512, NUL) == SHAPE
+    assert f(p(A + 8), 1024, p(A), 256, 512, NUL) == ALIGN and f(p(A), 1024, p(A + 2), 256, 512, NUL) == ALIGN
