@@ -270,8 +270,14 @@ def bench_attn(torch, q4w, synthetic, reps, t=262144, layers=16, ms=(1, 2, 3, 4,
         del outs, ws
     del caches
     torch.cuda.empty_cache()
+    m1 = per_m[str(ms[0])]
+    roof = {"bound": "hbm", "achieved": round(m1["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(m1["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("attn_decode_256k_traffic.json", attn_source_hash()),
+            "M": ms[0], "kernel": "attn_partial_kernel + attn_merge_kernel, one layer per launch pair",
+            "kernel_source_hash": attn_source_hash()}
     return dict(T=t, layers=layers, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
-                cache_bytes_per_layer=cache_bytes, per_M=per_m)
+                cache_bytes_per_layer=cache_bytes, per_M=per_m, roofline=roof)
 
 
 def bench_ceiling(torch, q4w, reps=40):
@@ -339,10 +345,11 @@ def bench_prefill_pass(torch, q4w, synthetic, reps, ms=(512, 1024, 2048)):
     return dict(layers=layers, launches_per_pass=7 * layers, per_M=per_m)
 
 
-def bench_prefill(torch, q4w, synthetic, reps):
+def bench_prefill(torch, q4w, synthetic, reps, gemm_only=False):
     """A8 route at M = 2048, one projection (K = 5120, N = 17408): the GEMM
     alone from prepared activations (the dominant kernel), then the whole
-    route per call (activation quantization + GEMM)."""
+    route per call (activation quantization + GEMM).  gemm_only: the GEMM
+    alone (one activation quantization in front), for profiling that kernel."""
     wl = synthetic.WORKLOADS["prefill_a8"]
     m, k, n = wl["M"], wl["K"], wl["N"]
     w = synthetic.weights_device(n, k, synthetic.WEIGHT_SEED)
@@ -354,12 +361,14 @@ def bench_prefill(torch, q4w, synthetic, reps):
     gemm = lambda: q4w.a8w4_gemm_prepared(ws, m, k, codes, scales, y)   # noqa: E731
     warm_clocks(torch, gemm)
     t_gemm = time_region(torch, lambda: [gemm() for _ in range(reps)], preroll=gemm) / reps
+    ops = 2 * m * n * k
+    if gemm_only:
+        return dict(M=m, K=k, N=n, ms_gemm=t_gemm * 1e3, tops_gemm=ops / t_gemm / 1e12)
     route = lambda: q4w.a8w4_gemm(x, codes, scales, y)                   # noqa: E731
     route()
     t_route = time_region(torch, lambda: [route() for _ in range(reps)], preroll=route) / reps
     t_quant = time_region(torch, lambda: [q4w.a8w4_prepare(x, ws) for _ in range(reps)],
                           preroll=lambda: q4w.a8w4_prepare(x, ws)) / reps
-    ops = 2 * m * n * k
     return dict(M=m, K=k, N=n, ms_route=t_route * 1e3, ms_gemm=t_gemm * 1e3, ms_act_quant=t_quant * 1e3,
                 one_projection_tokens_per_s=m / t_route,
                 tops_gemm=ops / t_gemm / 1e12, tops_route=ops / t_route / 1e12)
@@ -459,11 +468,16 @@ def source_hash(files):
 
 
 def kernel_source_hash():
-    return source_hash(("q4_gemv.hip", "q4w_internal.h"))
+    """The skinny kernel's own sources (the kernel, its plan and split-K fixup)."""
+    return source_hash(("q4_gemv.hip", "splitk.h"))
 
 
 def a8_source_hash():
-    return source_hash(("a8w4.hip", "q4w_internal.h"))
+    return source_hash(("a8w4.hip",))
+
+
+def attn_source_hash():
+    return source_hash(("q4_attn.hip",))
 
 
 def recorded_traffic(name, current_hash):
@@ -488,7 +502,8 @@ def main():
     ap.add_argument("--sections", default="decode,verify,step,attn,prefill,pass,ceiling",
                     help="comma list of extra sections (decode is always run)")
     ap.add_argument("--only", default=None,
-                    help="run only this section (decode, verify, step, attn, prefill, pass, ceiling) and print its "
+                    help="run only this section (decode, verify, step, attn, prefill, gemm (the A8 GEMM alone), pass, "
+                         "ceiling) and print its "
                          "result; for profiling one kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
@@ -524,6 +539,7 @@ def main():
               "prefill": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5)),
               "attn": lambda: bench_attn(torch, q4w, synthetic, reps=max(args.steps // 10, 3)),
               "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3),
+              "gemm": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5), gemm_only=True),
               "ceiling": lambda: bench_ceiling(torch, q4w)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
