@@ -210,27 +210,36 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
   // ---- the wave's V tile: key t's row holds its 256 channels as fp16 in
   // the dequantized pair order (column 8 i + (0, 2, 4, 6, 1, 3, 5, 7)[e] is
-  // channel 8 i + e); 16-byte chunk n of row t sits at chunk n ^ sw(t),
-  // sw(t) = 4 (t % 4) + (t / 4) % 4.
+  // channel 8 i + e); 16-byte chunk n of row t sits at chunk n ^ sw(t), with
+  // sw linear over the bits of t % 16: bit 0 -> 4, bit 1 -> 10, bit 2 -> 1,
+  // bit 3 -> 8.  Taken over 32 banks with 16 lanes per cycle, or over 64
+  // banks with 32 lanes per cycle (the conflict counter fits both), every
+  // transposed read (4 keys x 2 or 4 chunks) and every row write (8 or 16
+  // keys of one chunk) then touches distinct banks.
   const int vt = kQtBytes + wave * kVTile;
   // row writes: lane (key r, half hh) writes chunk 16 hh + c at wr ^ 16 c
-  const int wr = vt + r * kVRow + 256 * hh + 16 * (4 * (r & 3) + ((r >> 2) & 3));
+  const int wr = vt + r * kVRow + 256 * hh +
+                 16 * ((4 * (r & 1)) ^ (10 * ((r >> 1) & 1)) ^ ((r >> 2) & 1) ^ (8 * ((r >> 3) & 1)));
   // transposed reads (A operand of the 32 x 32 x 16 product): lane l takes
   // column 32 dt + l % 32 of keys 16 cp + 8 (l / 32) + 4 j + (0..3).  Within
   // each 16-lane group, lane 4 k + i / 4 reads the 8 bytes that the
-  // transpose hands to lane i as its element k: key 4 j + ((l >> 2) & 3),
-  // columns 4 (l & 3) + (0..3) of the group's 16.  The address for dt % 4 = e
-  // is rd[j] + 64 (e ^ x); cp and dt / 4 only add constants (8192 cp + 256 (dt / 4)).
-  const int x64 = 64 * ((lane >> 2) & 3);
+  // transpose hands to lane i as its element k: key 4 j + x (x = (l >> 2) & 3),
+  // columns 4 (l & 3) + (0..3) of the group's 16, i.e. logical chunk
+  // 4 dt + 2 grp + b (grp = (l >> 4) & 1, b = (l & 3) >> 1).  The key's
+  // bits are x (0-1), j (2) and l / 32 (3), so that chunk sits at
+  // 16 (dt / 4) + 4 ((dt % 4) ^ y) + 2 (grp ^ (x >> 1)) + (b ^ j) with
+  // y = (x & 1) + 2 ((x >> 1) ^ (l / 32)): the address for dt % 4 = e is
+  // rd[j] + 64 (e ^ y); cp and dt / 4 only add constants (8192 cp + 256 (dt / 4)).
+  const int y64 = 64 * ((((lane >> 2) & 3) & 1) | (((((lane >> 2) & 3) >> 1) ^ (lane >> 5)) << 1));
   int rd[2];
   {
+    const int x = (lane >> 2) & 3;
     const int grp = (lane >> 4) & 1;
+    const int bsel = (lane & 3) >> 1;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int u = (2 * (lane >> 5) + j) & 3;
-      rd[j] = vt + (8 * (lane >> 5) + 4 * j) * kVRow + x64 * (kVRow / 64) +
-              16 * ((2 * grp + ((lane & 3) >> 1)) ^ u) + 8 * (lane & 1);
-    }
+    for (int j = 0; j < 2; ++j)
+      rd[j] = vt + (8 * (lane >> 5) + 4 * j + x) * kVRow + 32 * (grp ^ (x >> 1)) + 16 * (bsel ^ j) +
+              8 * (lane & 1);
   }
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   lds_u8* const lds3 = (lds_u8*)lds;
@@ -273,7 +282,7 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       int b = rd[j];
       asm volatile("" : "+v"(b));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ra[j][e] = b + (x64 ^ (64 * e));
+      for (int e = 0; e < 4; ++e) ra[j][e] = b + (y64 ^ (64 * e));
     }
     auto load_a = [&](int idx) {                  // product idx: cp = idx / 8, dt = idx % 8
       const int dt = idx & 7;
