@@ -524,11 +524,23 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
 
   if constexpr (!kSplit) {
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs,
-    // so give each XCD a contiguous range of tiles (one weight tile is
-    // re-used across all token tiles inside one XCD's L2).
+    // so give each XCD its own tiles, which then share its L2.  With whole
+    // weight columns per XCD and at least 16 token tiles, an XCD walks its
+    // columns in two halves of the token tiles: its 64 resident workgroups
+    // then cover 8 columns x 8 token tiles (a smaller working set per K
+    // chunk than 4 columns x 16 token tiles; measured at M = 2048, N = 17408:
+    // L2 misses -39%, 0.380 -> 0.375 ms).  Otherwise a contiguous range of
+    // tiles per XCD.
     const int total = mtiles * ntiles;
     int bid = blockIdx.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    if ((ntiles & 7) == 0 && mtiles >= 16 && (mtiles & 1) == 0) {
+      const int x = bid & 7, i = bid >> 3;
+      const int cols = ntiles >> 3, gm = mtiles >> 1;
+      const int half = i / (cols * gm), rem = i - half * cols * gm;
+      bid = (x * cols + rem / gm) * mtiles + half * gm + rem % gm;
+    } else if ((total & 7) == 0) {
+      bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    }
     segment(bid, 0, nchunks);
     if (!kDebug) store_y(bid, own);
   } else {
