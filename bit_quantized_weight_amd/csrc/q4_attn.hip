@@ -156,12 +156,18 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
       (void*)v_scales, 0, T * row_scales * 2, kRsrcWord3);
   const uint32_t lane_codes = (uint32_t)(g * (kD / 2) + 64 * hh);      // + key * row_codes
   const uint32_t lane_scales = (uint32_t)((g * (kD / kBlock) + 4 * hh) * 2);
+  const uint32_t vlane_codes = (uint32_t)(g * (kD / 2) + kBlockBytes * (lane >> 3));   // V: block l >> 3
+  const uint32_t vlane_scales = (uint32_t)((g * (kD / kBlock) + (lane >> 3)) * 2);
 
-  // this lane's 64 code bytes and 4 block scales (fp16 x 4) of K, two tiles'
-  // worth (the next tile's are requested before this one is used), and of V
-  // (the next tile's are requested as soon as this one sits in LDS)
-  uint4 kc[2][4], vc[4];
-  v2u ksc[2], vsc;
+  // K: this lane's 64 code bytes and 4 block scales (fp16 x 4); the next
+  // tile's are requested as soon as this tile's scores are issued.  V: load i
+  // gives this lane the 16 code bytes (one block) of key 8 i + (l & 7), block
+  // l >> 3, and that block's scale, so each load covers 8 whole 128-byte
+  // lines (in the operand layout of K a load touches 32); the next tile's are
+  // requested as soon as this one sits in LDS.
+  uint4 kc[4], vc[4];
+  v2u ksc;
+  uint32_t vsc[4];
   auto load_k = [&](int k, uint4 (&kc)[4], v2u& ksc) {
     const int key = phys(k) * kTileKeys + r;
     const bool live = exists(k) && key < T;
@@ -175,16 +181,17 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     ksc = __builtin_amdgcn_raw_buffer_load_b64(rks, os, 0, 0);
   };
   auto load_v = [&](int k) {
-    const int key = phys(k) * kTileKeys + r;
-    const bool live = exists(k) && key < T;
-    const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
-    const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
+    const bool tile_live = exists(k);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 16 * i, 0);
+      const int key = phys(k) * kTileKeys + 8 * i + (lane & 7);
+      const bool live = tile_live && key < T;
+      const uint32_t oc = live ? (uint32_t)key * row_codes + vlane_codes : kOutOfRange;
+      const uint32_t os = live ? (uint32_t)key * row_scales * 2 + vlane_scales : kOutOfRange;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 0, 0);
       vc[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      vsc[i] = __builtin_amdgcn_raw_buffer_load_b16(rvs, os, 0, 0);
     }
-    vsc = __builtin_amdgcn_raw_buffer_load_b64(rvs, os, 0, 0);
   };
   auto scale2 = [](v2u s, int b) {          // block b (0..3) of the lane's 4 scales, as a pair
     const uint32_t w = b < 2 ? s[0] : s[1];
@@ -217,9 +224,17 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   // transposed read (4 keys x 2 or 4 chunks) and every row write (8 or 16
   // keys of one chunk) then touches distinct banks.
   const int vt = kQtBytes + wave * kVTile;
-  // row writes: lane (key r, half hh) writes chunk 16 hh + c at wr ^ 16 c
-  const int wr = vt + r * kVRow + 256 * hh +
-                 16 * ((4 * (r & 1)) ^ (10 * ((r >> 1) & 1)) ^ ((r >> 2) & 1) ^ (8 * ((r >> 3) & 1)));
+  // row writes: V load i of this lane (key t = 8 i + u, u = l & 7, block p =
+  // l >> 3) fills logical chunks 4 p + w (w = 0..3) of row t; sw(t) is
+  // sw(u) ^ 8 (i & 1), so the address is (wr[i & 1] + 4096 i) ^ 16 w.
+  int wr[2];
+  {
+    const int u = lane & 7, p = lane >> 3;
+    const int su = (4 * (u & 1)) ^ (10 * ((u >> 1) & 1)) ^ ((u >> 2) & 1);
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip)
+      wr[ip] = vt + u * kVRow + 16 * ((4 * p) ^ ((su ^ (8 * ip)) & 12)) + 16 * (su & 3);
+  }
   // transposed reads (A operand of the 32 x 32 x 16 product): lane l takes
   // column 32 dt + l % 32 of keys 16 cp + 8 (l / 32) + 4 j + (0..3).  Within
   // each 16-lane group, lane 4 k + i / 4 reads the 8 bytes that the
@@ -244,20 +259,25 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   lds_u8* const lds3 = (lds_u8*)lds;
 
-  // one tile; kcur holds its K, the next tile's K goes into knext.  The
+  // one tile; kc holds its K, then the next tile's.  The
   // scheduling fences keep each LDS operand read three products ahead of its
   // use (the compiler would otherwise issue it just before the product).
-  auto process = [&](int k, const uint4 (&kcur)[4], const v2u& kscur, uint4 (&knext)[4], v2u& ksnext) {
-    load_k(k + kWaves, knext, ksnext);            // next tile of this wave (past the end: zeros)
+  auto process = [&](int k) {
     const int t0 = phys(k) * kTileKeys;
-    // ---- V: dequantize this lane's half row into the wave's LDS tile ------
-    int w = wr;
-    asm volatile("" : "+v"(w));                   // addresses made per tile, not held in registers
+    // ---- V: dequantize this lane's 4 blocks into the wave's LDS tile ------
+    int wa[2] = {wr[0], wr[1]};
+    asm volatile("" : "+v"(wa[0]), "+v"(wa[1]));  // addresses made per tile, not held in registers
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint4 p = dequant8(word(vc, c), scale2(vsc, c >> 2));
-      *reinterpret_cast<uint4*>(lds + (w ^ (16 * c))) = p;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sb = vsc[i] & 0xFFFFu;
+      const h2 d2 = as_h2(sb | (sb << 16));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint4 p = dequant8(word(vc, 4 * i + w), d2);
+        *reinterpret_cast<uint4*>(lds + ((wa[i & 1] + 4096 * i) ^ (16 * w))) = p;
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);            // the next V codes reuse these registers
     load_v(k + kWaves);                           // next tile of this wave (past the end: zeros)
 
     // ---- scores S^T[t, r] ---------------------------------------------------
@@ -265,15 +285,16 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
     uint4 bq[4];
 #pragma unroll
     for (int c = 0; c < 3; ++c) bq[c] = qt[c * 64 + lane];
-    uint4 a = dequant8(word(kcur, 0), scale2(kscur, 0));
+    uint4 a = dequant8(word(kc, 0), scale2(ksc, 0));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
       if (c + 3 < 16) bq[(c + 3) & 3] = qt[(c + 3) * 64 + lane];
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(bq[c & 3]), s, 0, 0, 0);
-      if (c + 1 < 16) a = dequant8(word(kcur, c + 1), scale2(kscur, (c + 1) >> 2));
+      if (c + 1 < 16) a = dequant8(word(kc, c + 1), scale2(ksc, (c + 1) >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
+    load_k(k + kWaves, kc, ksc);                  // next tile of this wave (past the end: zeros)
 
     // ---- V^T operands of the first three value products (read ahead) ------
     int ra[2][4];
@@ -354,14 +375,11 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
 
   int k = wave;                                 // this wave's tiles: k, k + 8, ... of the slice
   if (exists(k)) {
-    load_k(k, kc[0], ksc[0]);
+    load_k(k, kc, ksc);
     load_v(k);
   }
 #pragma unroll 1
-  for (; exists(k); k += 2 * kWaves) {
-    process(k, kc[0], ksc[0], kc[1], ksc[1]);
-    if (exists(k + kWaves)) process(k + kWaves, kc[1], ksc[1], kc[0], ksc[0]);
-  }
+  for (; exists(k); k += kWaves) process(k);
   l_run += __shfl_xor(l_run, 32, 64);
 
   // ---- combine the 8 waves in LDS (the V tiles are free now) ----------------
