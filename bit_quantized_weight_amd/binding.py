@@ -122,6 +122,17 @@ def _need_shape(t, shape, name):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _need_packed(codes, scales, n, k, what="weights"):
+    """codes uint8 [n, k/2] and scales fp16 [n, k/32], contiguous CUDA tensors:
+    the library reads exactly these sizes, so a mismatch is refused here."""
+    import torch
+    _need(codes, torch.uint8, f"{what} codes")
+    _need(scales, torch.float16, f"{what} scales")
+    if k % 32 == 0:
+        _need_shape(codes, (n, k // 2), f"{what} codes")
+        _need_shape(scales, (n, k // 32), f"{what} scales")
+
+
 # Workspaces are cached per (route, device, stream): calls on one stream run
 # in order, so they may share one; calls on two streams could overlap in time
 # and must not (their split-K counters, partials and quantized activations
@@ -161,8 +172,10 @@ def q4_gemv_skinny_raw(x, codes, scales, y, split_k=0, ws=None):
     and, optionally, workspace ws (uint8; its whole size is passed, so the
     library rejects one that is too small)."""
     import torch
+    _need(x, torch.float16, "x")
     m, k = x.shape
     n = codes.shape[0]
+    _need_packed(codes, scales, n, k)
     _need(y, torch.float16, "y")
     _need_shape(y, (m, n), "y")
     if ws is None:
@@ -196,10 +209,9 @@ def gemv_noalloc(x, codes, scales, y, split_k=0):
     scratch holds the split-K state)."""
     import torch
     _need(x, torch.float16, "x")
-    _need(codes, torch.uint8, "codes")
-    _need(scales, torch.float16, "scales")
     m, k = x.shape
     n = codes.shape[0]
+    _need_packed(codes, scales, n, k)
     _need(y, torch.float16, "y")
     _need_shape(y, (m, n), "y")
     _check("q4_gemv_skinny_noalloc", lib().q4_gemv_skinny_noalloc(
@@ -222,6 +234,8 @@ def attn_decode(q, k_codes, k_scales, v_codes, v_scales, n_kv_heads, out=None, w
         _need(t, dt, name)
     m, hq, d = q.shape
     t_len = k_codes.shape[0]
+    _need_packed(k_codes, k_scales, t_len, n_kv_heads * d, "K cache")
+    _need_packed(v_codes, v_scales, t_len, n_kv_heads * d, "V cache")
     if out is None:
         out = torch.empty_like(q)
     _need(out, torch.float16, "out")
@@ -258,6 +272,7 @@ def a8w4_gemm(x, codes, scales, y=None):
     _need(x, torch.float16, "x")
     m, k = x.shape
     n = codes.shape[0]
+    _need_packed(codes, scales, n, k)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float16, device=x.device)
     _need(y, torch.float16, "y")
@@ -285,6 +300,7 @@ def a8w4_gemm_prepared(ws, m, k, codes, scales, y=None):
     """A8 GEMM from a workspace filled by a8w4_prepare -> fp16 Y [M, N]."""
     import torch
     n = codes.shape[0]
+    _need_packed(codes, scales, n, k)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float16, device=codes.device)
     _need(y, torch.float16, "y")
@@ -301,6 +317,7 @@ def a8w4_debug_block_acc(x, codes, scales):
     _need(x, torch.float16, "x")
     m, k = x.shape
     n = codes.shape[0]
+    _need_packed(codes, scales, n, k)
     acc = torch.empty((m, n, k // 32), dtype=torch.int32, device=x.device)
     nb = a8w4_ws_bytes(m, k)
     ws = _workspace(nb, x.device, "a8")
@@ -345,6 +362,8 @@ def batched_plan(items):
         _need(y, torch.float16, "y")
         if x.shape[0] != m or y.shape[0] != m:
             raise ValueError("every matmul of a batch has the same M")
+        _need_packed(codes, scales, codes.shape[0], x.shape[1])
+        _need_shape(y, (m, codes.shape[0]), "y")
     descs = _descs(items)
     nb = lib().q4_gemv_batched_ws_bytes(m, descs, len(items))
     if nb == 0:
