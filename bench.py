@@ -23,6 +23,8 @@ front.  Extra sections, each timed the same way, cover the rest of the path:
                          320-launch graph, and M = 1, 4, 5 as one persistent launch
   attn_decode_256k       the K/V reads of a step's 16 attention layers at a 262,144-token
                          4-bit cache, M = 1..5
+  decode_step_256k       a whole step at that context: the 64 layers' weights (one
+                         persistent launch) plus the 16 layers' K/V reads, M = 5 and 1
   a8w4_prefill           M = 2048, K = 5120, N = 17408 (activation quant + int8 MFMA GEMM)
   a8w4_prefill_pass_64L  the 64-layer A8 pass at M = 512, 1024 and 2048
   read_ceiling           a plain streaming read (q4w_stream_read) of the same byte
@@ -280,6 +282,56 @@ def bench_attn(torch, q4w, synthetic, reps, t=262144, layers=16, ms=(1, 2, 3, 4,
                 cache_bytes_per_layer=cache_bytes, per_M=per_m, roofline=roof)
 
 
+def bench_step_256k(torch, q4w, synthetic, reps=5, ms=(5, 1), t=262144, attn_layers=16):
+    """One whole decode step at a 262,144-token context: the weights of all 64
+    layers in one persistent launch, then the K/V reads of the 16
+    full-attention layers (one launch pair each), back to back on one stream.
+    The two HBM streams of a long-context step; the pages measure their sum as
+    the drop from about 50 to 12.61 tok/s when the cache fills."""
+    from bit_quantized_weight_amd.decode import DecodeStep
+    hq, hkv, d = 20, 4, 256
+    caches = []
+    for layer in range(attn_layers):
+        kv = []
+        for which in range(2):
+            w = synthetic.weights_device(t, hkv * d, 50_000 + 2 * layer + which, std=1.0)
+            kv.extend(q4w.pack(w))
+            del w
+        caches.append(kv)
+    cache_bytes = attn_layers * 2 * int(t * hkv * d * BYTES_PER_WEIGHT)
+    out = {}
+    base = None
+    for m in ms:
+        step = DecodeStep(m, weights=None if base is None else base.layers)
+        step.plan_batched()
+        q = synthetic.activations_device(m * hq, d, 60_000 + m).reshape(m, hq, d)
+        outs = [torch.empty_like(q) for _ in range(attn_layers)]
+        ws = torch.empty(max(q4w.attn_decode_ws_bytes(m, hq, hkv, d, t), 1), dtype=torch.uint8, device="cuda")
+
+        def run():
+            step.run_batched()
+            for (kc, ks, vc, vs), o in zip(caches, outs):
+                q4w.attn_decode(q, kc, ks, vc, vs, hkv, out=o, ws=ws)
+
+        torch.cuda.synchronize()
+        if base is None:
+            warm_clocks(torch, run)
+        run()
+        dt = time_region(torch, lambda: [run() for _ in range(reps)], preroll=run) / reps
+        total = step.weight_bytes + step.io_bytes + cache_bytes
+        out[str(m)] = dict(M=m, ms_step=dt * 1e3, steps_per_s=1 / dt, bytes_per_step=total,
+                           gbs=total / dt / 1e9, frac_of_peak=total / dt / 1e9 / HBM_PEAK_GBS,
+                           weight_bytes=step.weight_bytes, kv_bytes=cache_bytes)
+        del outs, ws
+        if base is None:
+            base = step
+        else:
+            del step
+    del base, caches
+    torch.cuda.empty_cache()
+    return dict(T=t, attn_layers=attn_layers, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, per_M=out)
+
+
 def bench_ceiling(torch, q4w, reps=40):
     """What a plain streaming read (q4w_stream_read) reaches on this GPU for
     the byte counts of the HBM-bound workloads: one decode_gate_up launch
@@ -499,11 +551,11 @@ def main():
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sections", default="decode,verify,step,attn,prefill,pass,ceiling",
+    ap.add_argument("--sections", default="decode,verify,step,attn,step256k,prefill,pass,ceiling",
                     help="comma list of extra sections (decode is always run)")
     ap.add_argument("--only", default=None,
-                    help="run only this section (decode, verify, step, attn, prefill, gemm (the A8 GEMM alone), pass, "
-                         "ceiling) and print its "
+                    help="run only this section (decode, verify, step, attn, step256k, prefill, gemm (the A8 GEMM "
+                         "alone), pass, ceiling) and print its "
                          "result; for profiling one kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (scale for HBM byte counters)")
@@ -540,7 +592,8 @@ def main():
               "attn": lambda: bench_attn(torch, q4w, synthetic, reps=max(args.steps // 10, 3)),
               "pass": lambda: bench_prefill_pass(torch, q4w, synthetic, reps=3),
               "gemm": lambda: bench_prefill(torch, q4w, synthetic, reps=max(args.steps, 5), gemm_only=True),
-              "ceiling": lambda: bench_ceiling(torch, q4w)}[args.only]
+              "ceiling": lambda: bench_ceiling(torch, q4w),
+              "step256k": lambda: bench_step_256k(torch, q4w, synthetic)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
 
@@ -566,6 +619,10 @@ def main():
         p = extra["a8w4_prefill"]
         log(f"[bench] a8w4_prefill: GEMM {p['ms_gemm']:.3f} ms, route {p['ms_route']:.3f} ms, "
             f"act quant {p['ms_act_quant']:.4f} ms")
+    if "step256k" in sections:
+        extra["decode_step_256k"] = bench_step_256k(torch, q4w, synthetic)
+        log("[bench] decode_step_256k:", {k_: round(v_["ms_step"], 3) for k_, v_ in extra["decode_step_256k"]["per_M"].items()},
+            "ms per step")
     if "ceiling" in sections:
         extra["read_ceiling"] = bench_ceiling(torch, q4w)
         log("[bench] read_ceiling:", {k_: round(v_["gbs"]) for k_, v_ in extra["read_ceiling"].items()}, "GB/s")
