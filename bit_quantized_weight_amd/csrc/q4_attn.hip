@@ -23,10 +23,12 @@
 //    keys of one query row: the row max and sum need one cross-half swap.
 //  * Softmax in base 2, in fp32, with a lazy running max: the output is
 //    rescaled only when some row's max grows by more than 8 (p <= 256).
-//  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  Each lane dequantizes its
-//    key's V half-row into a wave-private LDS tile (512-byte rows, 16-byte
-//    chunks XOR-swizzled by key so that neither the row writes nor the
-//    column reads meet bank conflicts); the product's V^T operand comes out
+//  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  The V codes are loaded 8
+//    lanes per key row (one 16-byte block each, so a load instruction covers
+//    8 whole cache lines) and dequantized into a wave-private LDS tile
+//    (512-byte rows, 16-byte chunks XOR-swizzled by key so that neither the
+//    row writes nor the column reads meet bank conflicts); the product's
+//    V^T operand comes out
 //    of that tile with the transposing LDS read (ds_read_b64_tr_b16: four
 //    keys of one channel per lane per read); P^T comes from the scores'
 //    registers through two v_permlane32_swap per 16 keys.
