@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -511,11 +512,19 @@ def cpu_baseline(synthetic, budget_s=4.0):
 # traffic counters recorded under profiles/ (valid only for the same kernel source)
 # --------------------------------------------------------------------------
 
+def code_text(text):
+    """Source text with comments and blank lines removed: a change to the
+    comments alone leaves the compiled kernel, and so its counters, as they were."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.split("\n") if line.strip()) + "\n"
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "bit_quantized_weight_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_quantized_weight_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
