@@ -233,7 +233,6 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
   __shared__ ChunkLds lds0, lds1;
   __shared__ uint4 rawq[kRawUnits];
   __shared__ int is_last;
-  typedef unsigned v4u __attribute__((ext_vector_type(4)));
   static_assert(kMS == 2 || kMS == 4, "64- or 128-row tiles");
   constexpr int TM = 32 * kMS;      // rows (tokens) of this workgroup's tile
   constexpr int kMI = kMS / 2;      // 32-row subtiles per wave
@@ -281,10 +280,6 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
         (void*)(codes + (size_t)n_base * nb), 0, rows_here * nb * kBlockBytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(xq_t + (size_t)mt32 * nb * 64), 0, kMS * nb * 64 * 16, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(sa_t + (size_t)mt32 * G * 32), 0, kMS * G * 32 * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(scales + (size_t)n_base * nb), 0, rows_here * nb * 2, 0x00020000);
 
     // ---- cooperative chunk staging ------------------------------------------
     // The weight codes (2 units (row, block) of 16 B per thread) and the
@@ -296,16 +291,16 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
     // nb, nb + 1 read the next row's first blocks (the buffer range check
     // gives zeros past the last row) and the activation loads the next
     // subtile's: finite values whose group is multiplied by d = 0, because
-    // the scale loads, like the activation-scale loads, are masked to zero
-    // past the last block.
+    // the scale loads, like the activation-scale loads, read zeros past the
+    // last block (a wave-uniform test gives them an empty buffer resource).
     uint32_t rawd;
     float rawsa;
     const uint32_t ob = (uint32_t)(((tid >> 2) * nb + (tid & 3)) * kBlockBytes);   // unit it: + it * 64 rows
     const uint32_t ob_rows = (uint32_t)(64 * nb * kBlockBytes);
     const uint32_t oa = (uint32_t)((wave * 64 + lane) * 16);
-    const int sgi = tid >> 7;                                  // scale pair: group of the chunk
+    const int sgi = wave >> 1;                                 // scale pair: group of the chunk (tid >> 7)
     const uint32_t od = (uint32_t)(((tid & 127) * nb + 2 * sgi) * 2);
-    const int agi = tid / TM;                                  // activation scale: group of the chunk
+    const int agi = (wave * 64) / TM;                          // activation scale: group of the chunk (tid / TM)
     const uint32_t osa = (uint32_t)((((tid % TM) >> 5) * G * 32 + (tid & 31)) * 4);
     auto stage_issue = [&](int c, ChunkLds& L) {
   #pragma unroll
@@ -321,12 +316,15 @@ a8w4_gemm_kernel(const uint4* __restrict__ xq_t, const float* __restrict__ sa_t,
             ra, (lds_ptr_t)(&L.aq[(it * kChunkBlocks + wave) * 64]), 16, oa,
             (it * nb + c * kChunkBlocks) * 64 * 16, 0, 0);
       if (!kDebug) {
-        const bool dlive = c * kChunkBlocks + 2 * sgi < nb;
-        rawd = __builtin_amdgcn_raw_buffer_load_b32(rsc, dlive ? od + c * kChunkBlocks * 2 : 0x80000000u, 0, 0);
+        const bool dlive = c * kChunkBlocks + 2 * sgi < nb;     // wave-uniform
+        const __amdgpu_buffer_rsrc_t rsd = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(scales + (size_t)n_base * nb), 0, dlive ? rows_here * nb * 2 : 0, 0x00020000);
+        rawd = __builtin_amdgcn_raw_buffer_load_b32(rsd, od, c * kChunkBlocks * 2, 0);
         const int g = c * kChunkGroups + agi;
-        const bool alive = agi < kChunkGroups && g < G;
-        rawsa = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rsa, alive ? osa + g * 32 * 4 : 0x80000000u, 0, 0));
+        const bool alive = agi < kChunkGroups && g < G;        // wave-uniform
+        const __amdgpu_buffer_rsrc_t rsl = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(sa_t + (size_t)mt32 * G * 32), 0, alive ? kMS * G * 32 * 4 : 0, 0x00020000);
+        rawsa = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, osa, g * 32 * 4, 0));
       }
     };
     // Waits for the chunk's loads (the raw codes a thread unpacks are the
