@@ -456,7 +456,9 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
   // One register set: a unit's codes and scales.  Scales with kScaleQuad:
   // lane group g loads the 4 scales of step 4l + g of its row (8 bytes), one
   // load per 4 steps; the groups' words are all-gathered with permlane swaps
-  // at compute time.  Otherwise four 2-byte loads per step.
+  // at compute time.  Otherwise four 2-byte loads per step.  The scales are
+  // requested before the codes, so the first step's products and scale FMAs
+  // wait for its own codes only, not for the whole unit.
   static_assert(P % kBlocksPerStep == 0, "scale loads cover 4 steps each");
   constexpr int kScaleLoads = P / kBlocksPerStep;
   struct Set {
@@ -490,13 +492,6 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
       }
     }
     const uint32_t vrow = (uint32_t)(rl * nb + kb0);
-#pragma unroll
-    for (int t = 0; t < P; ++t) {
-      const bool live = t * kBlocksPerStep + grp < nbs;
-      const uint32_t vo = live ? (vrow + grp) * kBlockBytes : kOutOfRange;
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kBlocksPerStep * kBlockBytes, 0);
-      st.w[t] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
     if constexpr (kScaleQuad) {
 #pragma unroll
       for (int l = 0; l < kScaleLoads; ++l) {
@@ -514,6 +509,13 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
         for (int j = 0; j < kBlocksPerStep; ++j)
           st.s[t][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, so, t * kBlocksPerStep * 2 + 2 * j, 0);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      const bool live = t * kBlocksPerStep + grp < nbs;
+      const uint32_t vo = live ? (vrow + grp) * kBlockBytes : kOutOfRange;
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, t * kBlocksPerStep * kBlockBytes, 0);
+      st.w[t] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   // Value of lane group g's v in every lane: out[g].
