@@ -653,7 +653,11 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
         }
         compute(cw, sets[u % kSets], lds0 + parity * kLdsBuf, yacc[u]);
         const Walker nw = advance(w[(u + kSets - 1) % kSets]);
+        // the unit's loads go out at raised wave priority, ahead of the
+        // other waves' arithmetic on this SIMD (-0.3 to -0.8% per step)
+        __builtin_amdgcn_s_setprio(2);
         issue(nw, sets[u % kSets], (u + kSets) % T == 0);   // tile 0 of the next chunk
+        __builtin_amdgcn_s_setprio(0);
         cw = nw;
       }
     }
