@@ -277,6 +277,26 @@ def test_large_n_split_counters(m):
     assert_close(y[:, rows], q4.matmul(x, q, d), what=f"N={n} M={m} split 2")
 
 
+@pytest.mark.parametrize("m", [1, 5])
+def test_max_k(m):
+    """K at the entry point's limit (2^24, 524,288 blocks per row) over 40 rows:
+    the longest rows the library accepts, split into many slices; the byte
+    offsets of the last row's blocks and of the activations are the largest
+    any kernel forms.  Sampled rows (both ends included) against the oracle."""
+    torch = torch_cuda()
+    n, k = 40, 1 << 24
+    w = synthetic.weights_device(n, k, 87)
+    rows = np.array([0, 17, n - 1])
+    wr = w.index_select(0, torch.as_tensor(rows, device="cuda")).cpu().numpy()
+    codes, scales = pack(w)
+    del w
+    q, d = q4.quantize(wr)
+    x = synthetic.activations_device(m, k, 88 + m)
+    y = gemv(x, codes, scales)
+    torch.cuda.synchronize()
+    assert_close(host(y)[:, rows], q4.matmul(host(x), q, d), what=f"M={m} N={n} K={k}")
+
+
 @functools.lru_cache(maxsize=2)
 def packed_sampled(n, k, seed, rows):
     """Weights generated and packed on the GPU; the oracle quantizes only the
