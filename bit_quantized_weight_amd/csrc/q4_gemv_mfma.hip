@@ -63,16 +63,34 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kBlocksPerStep = 4;            // one 128-bit load per lane = 4 blocks per lane group set
 constexpr int kMaxSliceSteps = 8;            // K-slice cap: 32 blocks
+// Row map of the products.  Lane group g holds D rows 4 g .. 4 g + 3 and
+// applies the block scale to each of them that holds an activation row.  Up
+// to M = 8, activation row m is row mfma_row = 4 (m % 4) + m / 4 of A and D
+// (a 4 x 4 transpose of the row index, its own inverse): group g holds rows
+// g, g + 4 of the activations, so a lane scales d_rows = ceil(M / 4) D rows
+// (one at M <= 4, where rows 0..3 in order would take min(M, 4)).  Past
+// M = 8 the rows stay in order (four D rows per lane either way).  Row r of
+// a product depends on A row r only, so any row map gives the same values.
+__host__ __device__ constexpr bool rows_transposed(int M) { return M <= 8; }
+__host__ __device__ constexpr int mfma_row(int M, int m) {
+  return rows_transposed(M) ? 4 * (m & 3) + (m >> 2) : m;
+}
+__host__ __device__ constexpr int d_rows(int M) { return rows_transposed(M) ? (M + 3) / 4 : 4; }
+// Lane group g's D rows hold at least one activation row.
+__host__ __device__ constexpr bool group_live(int M, int g) { return rows_transposed(M) ? g < M : 4 * g < M; }
+// Activation row held by D row r of lane group g.
+__host__ __device__ constexpr int act_row(int M, int g, int r) { return rows_transposed(M) ? g + 4 * r : 4 * g + r; }
+// -bias floats per block, indexed by MFMA row: lane group g reads rows
+// 4 g .. 4 g + 3 (at M = 1 only group 0 has a real row).
+__host__ __device__ constexpr int bias_slots(int M) { return M == 1 ? 4 : rows_transposed(M) ? 16 : (M + 3) / 4 * 4; }
 // LDS per block of the slice: the M activation rows as A-operand octets
-// (4 slot groups x M rows x 16 bytes) and the -bias of rows 0..Mp4-1
-// (Mp4 = M rounded up to 4; rows >= M hold 0).  A-operand rows M..15 are
-// not stored: their lanes read row 0's octets instead.  Row m of an MFMA
-// product depends on A row m only, and rows >= M are never stored, so what
-// those lanes read does not matter; reading in-bounds data at the same
-// stride as every other lane keeps each LDS address a per-lane base plus a
-// constant offset.
+// (4 slot groups x M rows x 16 bytes) and the -bias of each MFMA row that
+// holds an activation (the other slots are never written: the D rows they
+// start are never stored).  A-operand rows that hold no activation are not
+// stored either: their lanes read activation row 0's octets instead, which
+// keeps each LDS address a per-lane base plus a constant offset.
 __host__ __device__ constexpr int mp4(int M) { return (M + 3) / 4 * 4; }
-__host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * mp4(M); }
+__host__ __device__ constexpr int lds_bytes_per_block(int M) { return 64 * M + 4 * bias_slots(M); }
 // Steps of a K-chunk whose (block, row) staging items fit kItems per thread,
 // at most kMaxSliceSteps.  The streaming kernel stages one item per thread;
 // the single-launch kernel up to two (8 steps for every M <= 16).
@@ -142,7 +160,7 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   constexpr int R = mfma_tiles_per_wave(M);
   constexpr int P = mfma_ring_steps(M);
   constexpr int kRowsPerWg = kWaves * R * 16;
-  constexpr int RM = M < 4 ? M : 4;          // D rows a lane accumulates
+  constexpr int RM = d_rows(M);              // D rows a lane accumulates
 
   const int nb = K / kBlock;
   const int tid = threadIdx.x;
@@ -226,11 +244,11 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int p = 0; p < P; ++p) load_step(p, buf[p], sbuf[p]);
 
-  // ---- stage A operands and biases: xs[b][g][m] (m < M), cl[b][m] ---------
+  // ---- stage A operands and biases: xs[b][g][m] (m < M), cl[b][mfma_row(m)] -
   __syncthreads();   // the previous item of this workgroup is done with the LDS
   char* lds = reinterpret_cast<char*>(smem);
   uint4* xs = smem;                                                    // [bpad][4][M]
-  float* cl = reinterpret_cast<float*>(lds + bpad * 64 * M);           // [bpad][MP]
+  float* cl = reinterpret_cast<float*>(lds + bpad * 64 * M);           // [bpad][bias_slots]
   const uint32_t k1032 = 0x64086408u;
   const uint32_t k72 = 0x54805480u;
 #pragma unroll
@@ -254,19 +272,21 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
         c = dot2(o.z, k1032, c);
         c = dot2(o.w, k72, c);
       }
-      cl[sb * MP + sm] = -c;               // rows >= M read zeros, so c == 0 there
+      if (sm < M) cl[sb * bias_slots(M) + mfma_row(M, sm)] = -c;
     }
   }
   __syncthreads();
 
   // Per-lane LDS addresses: A octet of block b at a_base + b * a_stride
-  // (rows >= M read row 0), bias float4 of rows 4 grp.. at c_base +
-  // b * c_stride (groups past Mp4 read group 0's).  The strides are
-  // constants, so the compiler folds b * stride into the LDS instruction.
-  const int a_base = (grp * M + (col < M ? col : 0)) * 16;
+  // (MFMA rows without an activation read row 0's), bias float4 of MFMA rows
+  // 4 grp.. at c_base + b * c_stride (groups without a real row read group
+  // 0's).  The strides are constants, so the compiler folds b * stride into
+  // the LDS instruction.
+  const int am = mfma_row(M, col);
+  const int a_base = (grp * M + (am < M ? am : 0)) * 16;
   constexpr int a_stride = 64 * M;
-  const int c_base = bpad * 64 * M + (4 * grp < MP ? grp : 0) * 16;
-  constexpr int c_stride = MP * 4;
+  const int c_base = bpad * 64 * M + (group_live(M, grp) ? grp : 0) * 16;
+  constexpr int c_stride = bias_slots(M) * 4;
 
   f4 yacc[R];
 #pragma unroll
@@ -318,13 +338,13 @@ __device__ __forceinline__ void mfma_item(const uint16_t* __restrict__ x,
   for (int p = 0; p < P; ++p)
     if (p < steps) compute_step(p, buf[p], sbuf[p]);
 
-  // ---- store: lane (col, grp) holds rows 4 grp + r of its column ---------
+  // ---- store: lane (col, grp) holds activation rows act_row(grp, r) -------
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int n = tile_row0 + (wave * R + i) * 16 + col;
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      const int m = 4 * grp + r;
+      const int m = act_row(M, grp, r);
       if (m < M && n < N) {
         if (S == 1) y[(size_t)m * N + n] = __half_as_ushort(__float2half_rn(yacc[i][r]));
         else
@@ -405,7 +425,7 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
   constexpr int T = kStreamTiles;
   constexpr int kChunkBlocks = P * kBlocksPerStep;
   constexpr int MP = mp4(M);
-  constexpr int RM = M < 4 ? M : 4;
+  constexpr int RM = d_rows(M);
   constexpr int kLdsBuf = lds_bytes(M, kChunkBlocks);
   constexpr int kSets = 2;
   static_assert(T % kSets == 0, "units cycle through register sets and tiles together");
@@ -421,10 +441,11 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
   const int rl = wave * 16 + col;          // tile-local weight row of this lane
 
   // Per-lane LDS addresses (see mfma_item), for a buffer of kChunkBlocks blocks.
-  const int a_base = (grp * M + (col < M ? col : 0)) * 16;
+  const int am = mfma_row(M, col);
+  const int a_base = (grp * M + (am < M ? am : 0)) * 16;
   constexpr int a_stride = 64 * M;
-  const int c_base = kChunkBlocks * 64 * M + (4 * grp < MP ? grp : 0) * 16;
-  constexpr int c_stride = MP * 4;
+  const int c_base = kChunkBlocks * 64 * M + (group_live(M, grp) ? grp : 0) * 16;
+  constexpr int c_stride = bias_slots(M) * 4;
 
   // This workgroup's items, ascending: items[pos] for pos in [first, end).
   const uint32_t* items = sched + (kMaxBatchedGrid + 1);
@@ -551,7 +572,7 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
         c = dot2(o.z, 0x64086408u, c);
         c = dot2(o.w, 0x54805480u, c);
       }
-      cl[sb * MP + sm] = -c;
+      if (sm < M) cl[sb * bias_slots(M) + mfma_row(M, sm)] = -c;
     }
   };
 
@@ -613,7 +634,7 @@ mfma_stream_kernel(const BatchedGemv* __restrict__ table, int count, const uint3
       const int n = ((w.item - d.item_begin) * T + w.tile) * 64 + rl;
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
-        const int m = 4 * grp + r;
+        const int m = act_row(M, grp, r);
         if (m < M && n < d.N) d.y[(size_t)m * d.N + n] = __half_as_ushort(__float2half_rn(yacc[r]));
       }
       yacc = f4{0.f, 0.f, 0.f, 0.f};
