@@ -53,6 +53,26 @@ __device__ __forceinline__ int quant127(float x, float sa) {
   return (int)q;
 }
 
+// quant127 with the division replaced by a product with rs = v_rcp_f32(sa)
+// (1 ulp), rs = 0 when sa == 0.  Since |x / sa| <= 127.01, y = x rs is within
+// 2^-15 of the correctly rounded quotient v = fl(x / sa), so
+// round_half_away(y) = sign(y) floor(|y| + 1/2) equals round_half_away(v)
+// unless |y| + 1/2 lies within 2^-12 of an integer; there (about 0.05% of
+// elements) the correctly rounded division decides.
+__device__ __forceinline__ int quant127_rcp(float x, float sa, float rs) {
+  const float y = x * rs;
+  const float t = fabsf(y) + 0.5f;
+  const float fl = floorf(t);
+  const float f = t - fl;
+  if (fminf(f, 1.0f - f) < 0x1p-12f) return quant127(x, sa);
+  const float q = fminf(copysignf(fl, y), 127.0f);
+  return (int)fmaxf(q, -127.0f);
+}
+
+__device__ __forceinline__ float rcp_or_zero(float sa) {
+  return sa == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sa);
+}
+
 __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
   const uint4 r = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -91,11 +111,12 @@ __global__ void __launch_bounds__(256) act_quant_rowmajor_kernel(const uint16_t*
   a = fmaxf(a, __shfl_xor(a, 2, 8));
   a = fmaxf(a, __shfl_xor(a, 4, 8));
   const float s = a / 127.0f;
+  const float rs = rcp_or_zero(s);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= ((uint32_t)quant127(v[i], s) & 0xFFu) << (8 * i);
+  for (int i = 0; i < 4; ++i) lo |= ((uint32_t)quant127_rcp(v[i], s, rs) & 0xFFu) << (8 * i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= ((uint32_t)quant127(v[4 + i], s) & 0xFFu) << (8 * i);
+  for (int i = 0; i < 4; ++i) hi |= ((uint32_t)quant127_rcp(v[4 + i], s, rs) & 0xFFu) << (8 * i);
   if (live) {
     *reinterpret_cast<uint2*>(xq + off) = make_uint2(lo, hi);
     if (e == 0) sa[(size_t)m * G + g] = s;
@@ -149,13 +170,14 @@ __global__ void __launch_bounds__(64) act_quant_tiled_kernel(const uint16_t* __r
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[bi][i]));
   a = fmaxf(a, __shfl_xor(a, 32, 64));
   const float s = a / 127.0f;
+  const float rs = rcp_or_zero(s);
   constexpr int perm[16] = {0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15};
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
     uint32_t wv[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int sidx = 0; sidx < 16; ++sidx)
-      wv[sidx >> 2] |= ((uint32_t)quant127(v[bi][perm[sidx]], s) & 0xFFu) << (8 * (sidx & 3));
+      wv[sidx >> 2] |= ((uint32_t)quant127_rcp(v[bi][perm[sidx]], s, rs) & 0xFFu) << (8 * (sidx & 3));
     const int b = 2 * g + bi;
     xq_t[((size_t)mt * nb + b) * 64 + l] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }

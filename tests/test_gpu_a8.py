@@ -42,6 +42,43 @@ def test_act_quant_special():
     assert np.array_equal(host(sa).view(np.uint32), sa_ref.view(np.uint32))
 
 
+def _every_fp16_value(absmax):
+    """Rows of one 64-channel group: channel 0 holds absmax (so every group's
+    scale is sa = fl32(absmax / 127)), channels 1..63 run through every finite
+    fp16 value of magnitude at most absmax, both signs."""
+    a = np.float16(absmax)
+    pos = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    vals = pos[pos <= a]
+    vals = np.concatenate([vals, -vals])
+    n = -(-len(vals) // 63)
+    flat = np.zeros(n * 63, np.float16)
+    flat[:len(vals)] = vals
+    x = np.zeros((n, 64), np.float16)
+    x[:, 0] = a
+    x[:, 1:] = flat.reshape(n, 63)
+    return x
+
+
+@pytest.mark.parametrize("absmax", [127.0, 100.0, 37.5, 3.0, 0.001, 65504.0])
+def test_act_quant_every_fp16_value(absmax):
+    """Every fp16 activation against a fixed group scale: each value whose
+    quotient x / sa falls at or next to a rounding tie is met, so the
+    quantizers' fast path and its exact fallback are both checked, bit-exact
+    against the oracle (row-major quantizer directly; the GEMM's tiled
+    quantizer through the int32 block sums)."""
+    torch = torch_cuda()
+    x = _every_fp16_value(absmax)
+    xq, sa = a8_quantize_act(dev(x, torch))
+    torch.cuda.synchronize()
+    qa, sa_ref = a8.quantize_act(x)
+    assert np.array_equal(host(xq), qa)
+    assert np.array_equal(host(sa).view(np.uint32), sa_ref.view(np.uint32))
+    codes, scales, q, d = _packed(16, 64, 250)
+    acc = a8w4_debug_block_acc(dev(x, torch), codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), a8.block_sums(qa, q).astype(np.int32))
+
+
 @pytest.mark.parametrize("m,n,k", [(1, 32, 64), (31, 48, 256), (33, 130, 128), (128, 128, 512),
                                    (130, 257, 192), (256, 512, 5120)])
 def test_block_sums_bit_exact(m, n, k):
