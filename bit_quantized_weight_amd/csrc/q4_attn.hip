@@ -10,7 +10,10 @@
 // over the cache positions t <= T - M + m.  K and V are token-major rows of
 // H_kv * D values in the weights' 32-element 4-bit block format.
 //
-// gfx950 design (bound by streaming the cache from HBM):
+// gfx950 design (bound by streaming the cache from HBM).  Two forms of the
+// first kernel: up to R = 16 query rows per K/V head (one query token at
+// G = 5, up to three) the 16-row form below (attn16_partial_kernel, 16 x 16
+// x 32 products), above that the 32-row form described here:
 //  * One workgroup (8 waves) per (K/V head g, slice of the keys); a wave
 //    takes 32-key tiles of its slice in turn and keeps its own running max,
 //    sum and output (flash-decoding).  The R = M * G query rows of head g
@@ -57,6 +60,7 @@ constexpr int kMergeBatch = 16;           // slice loads in flight per thread in
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
@@ -447,6 +451,393 @@ attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ 
   }
 }
 
+// ---- kernel 1, 16-row form: R <= 16 (RT = 1) or 32 (RT = 2) -----------------
+// The same partial result on v_mfma_f32_16x16x32_f16, with the query rows in
+// RT tiles of 16 columns, so that R <= 16 (one query token at G = 5 up to
+// three) pays for 16 columns instead of 32.  Lane l: c = l % 16, grp = l / 16.
+//  * Scores S^T[t, r]: A = K rows (key 16 h + c of the tile's half h, slots
+//    8 grp ..), B = Q^T (column r = 16 rt + c), D rows 4 grp .. 4 grp + 3.
+//    Lane (c, grp) loads bytes [32 grp, 32 grp + 32) of its key's 128 (blocks
+//    2 grp and 2 grp + 1, so 4 lanes share each 128-byte line of a load
+//    instruction) and their two scales; product j takes code word j, that is
+//    channels 64 grp + 8 j .. 64 grp + 8 j + 7 in the dequantized pair order,
+//    and Q^T holds the same channels.
+//  * A lane ends with 4 keys x 2 halves of its query row: slot 8 grp + 4 h + i
+//    of the value product is key 16 h + 4 grp + i, so P^T, the B operand of
+//    O^T[d, r] += V^T[d, t] P^T[t, r], is the lane's own 8 probabilities.
+//  * V^T comes from the wave's LDS tile through two transposing reads per
+//    product (keys 4 grp + 0..3 and 16 + 4 grp + 0..3 of one channel).  Rows
+//    are 512 bytes; 16-byte chunk n of row t sits at n ^ f(t), f linear over
+//    the bits of t % 8 (bit 0 -> 2, bit 1 -> 5, bit 2 -> 9): the row writes
+//    (8 keys x 2 blocks per 16 lanes) and the transposing reads (8 keys x 2
+//    chunks per 32 lanes) then meet no bank conflicts, with 32 or 64 banks.
+//  * Lazy running max as in the 32-row form: the row max across a row's four
+//    lanes is taken only when some score passes its row's max by more than 8.
+__device__ __forceinline__ int vt_swizzle(int t) {   // f(t) on t % 8
+  return (2 * (t & 1)) ^ (5 * ((t >> 1) & 1)) ^ (9 * ((t >> 2) & 1));
+}
+
+// max of x over lanes l and l ^ 16
+__device__ __forceinline__ float rows16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int RT>
+__global__ void __launch_bounds__(kThreads)
+attn16_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+                      const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
+                      const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
+                      float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
+  static_assert(RT == 1 || RT == 2, "16 or 32 query rows");
+  constexpr int kQtEntries = RT * 8 * 64;                 // [rt][product j][lane] uint4
+  constexpr int kQt16Bytes = kQtEntries * 16;
+  constexpr int kLds16 = kQt16Bytes + kWaves * kVTile;
+  __shared__ __align__(16) unsigned char lds[kLds16];
+  uint4* qt = reinterpret_cast<uint4*>(lds);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  const int grp = lane >> 4;
+  const int split = blockIdx.x;
+  const int head = blockIdx.y;               // K/V head
+  const int G = Hq / Hkv;
+  const int R = M * G;
+  const int ntiles = (T + kTileKeys - 1) / kTileKeys;
+  const int S = gridDim.x;
+  auto phys = [&](int k) { return k * S + split; };
+  auto exists = [&](int k) { return k < tps && phys(k) < ntiles; };
+
+  // ---- Q^T into LDS: entry (rt, j, lane') = Q[16 rt + c', 64 grp' + 8 j + (0,4,1,5,2,6,3,7)]
+  for (int e = tid; e < kQtEntries; e += kThreads) {
+    const int l2 = e & 63, j = (e >> 6) & 7, rt = e >> 9;
+    const int r2 = 16 * rt + (l2 & 15), g2 = l2 >> 4;
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (r2 < R) {
+      const int m = r2 / G, hq = head * G + r2 % G;
+      const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)m * Hq + hq) * kD + 64 * g2 + 8 * j);
+      o.x = (w.x & 0xFFFFu) | (w.z << 16);          // (e0, e4)
+      o.y = (w.x >> 16) | (w.z & 0xFFFF0000u);      // (e1, e5)
+      o.z = (w.y & 0xFFFFu) | (w.w << 16);          // (e2, e6)
+      o.w = (w.y >> 16) | (w.w & 0xFFFF0000u);      // (e3, e7)
+    }
+    qt[e] = o;
+  }
+  __syncthreads();
+  uint4 bq1[RT == 1 ? 8 : 1];                      // one row tile: Q^T held in registers
+  if constexpr (RT == 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq1[j] = qt[j * 64 + lane];
+  }
+
+  const int row_codes = Hkv * kD / 2;
+  const int row_scales = Hkv * kD / kBlock;
+  // Each tile is read through buffer resources that start at the tile and end
+  // at the cache's end (no bytes for a tile that does not exist), so a lane's
+  // offsets are the same for every tile and the keys past T read zeros.
+  auto tile_rsrc = [&](const void* base, int k, int row_bytes) {
+    const bool live = exists(k);
+    const uint32_t off = live ? (uint32_t)phys(k) * kTileKeys * row_bytes : 0u;
+    const uint32_t n = live ? (uint32_t)T * row_bytes - off : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const unsigned char*>(base) + off), 0, n,
+                                             kRsrcWord3);
+  };
+  uint32_t kvo[2], kso[2], vvo[4], vso[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    kvo[h] = (uint32_t)((16 * h + c) * row_codes + head * (kD / 2) + 32 * grp);
+    kso[h] = (uint32_t)(((16 * h + c) * row_scales + head * (kD / kBlock) + 2 * grp) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vvo[i] = (uint32_t)((8 * i + (lane & 7)) * row_codes + head * (kD / 2) + kBlockBytes * (lane >> 3));
+    vso[i] = (uint32_t)(((8 * i + (lane & 7)) * row_scales + head * (kD / kBlock) + (lane >> 3)) * 2);
+  }
+
+  // K of half h: 32 code bytes (8 words) and 2 block scales of key 16 h + c.
+  // V load i: the 16 code bytes (one block) of key 8 i + (l & 7), block
+  // l >> 3, and its scale (8 whole 128-byte lines per load instruction).
+  uint4 kc[2][2], vc[4];
+  uint32_t ksc[2], vsc[4];
+  auto load_k = [&](int k) {
+    const __amdgpu_buffer_rsrc_t rkc = tile_rsrc(k_codes, k, row_codes);
+    const __amdgpu_buffer_rsrc_t rks = tile_rsrc(k_scales, k, row_scales * 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rkc, kvo[h], 16 * i, 0);
+        kc[h][i] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      ksc[h] = __builtin_amdgcn_raw_buffer_load_b32(rks, kso[h], 0, 0);
+    }
+  };
+  auto load_v = [&](int k) {
+    const __amdgpu_buffer_rsrc_t rvc = tile_rsrc(v_codes, k, row_codes);
+    const __amdgpu_buffer_rsrc_t rvs = tile_rsrc(v_scales, k, row_scales * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rvc, vvo[i], 0, 0);
+      vc[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      vsc[i] = __builtin_amdgcn_raw_buffer_load_b16(rvs, vso[i], 0, 0);
+    }
+  };
+  auto word = [](const uint4 (&v)[2], int i) {
+    const uint4 x = v[i >> 2];
+    const int j = i & 3;
+    return j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
+  };
+  auto bq = [&](int rt, int j) -> h8 {
+    if constexpr (RT == 1) return as_h8(bq1[j]);
+    else return as_h8(qt[(rt * 8 + j) * 64 + lane]);
+  };
+
+  // the last position query row 16 rt + c may see (rows past R: every key)
+  int lim[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + c;
+    lim[rt] = r < R ? T - M + r / G : T - 1;
+  }
+  const float c2 = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(D)
+
+  f4 o[RT][16];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RT], l_run[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_run[rt] = kNegBig;
+    l_run[rt] = 0.f;
+  }
+
+  // V tile addresses.  Row writes: V load i of lane (u = l & 7, b = l >> 3)
+  // fills chunks 4 b + w of row 8 i + u: (wr + 4096 i) ^ 16 w.  Transposing
+  // reads: lane (c, grp) addresses row 4 grp + c / 4 (+ 16 for the second
+  // read), chunk 2 dt + (c % 4) / 2, half c % 2, which is
+  // (rd ^ 32 (dt % 8)) + 256 (dt / 8) (+ 8192).
+  const int vt = kQt16Bytes + wave * kVTile;
+  const int wr = vt + (lane & 7) * kVRow + 16 * ((4 * (lane >> 3)) ^ vt_swizzle(lane & 7));
+  const int trow = 4 * grp + (c >> 2);
+  const int rd = vt + trow * kVRow + 16 * (((c & 3) >> 1) ^ vt_swizzle(trow)) + 8 * (c & 1);
+  int wrw[4], rdl[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wrw[w] = wr ^ (16 * w);
+#pragma unroll
+  for (int dl = 0; dl < 8; ++dl) rdl[dl] = rd ^ (32 * dl);
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  lds_u8* const lds3 = (lds_u8*)lds;
+
+  auto process = [&](int k) {
+    const int t0 = phys(k) * kTileKeys;
+    // ---- V: dequantize this lane's 4 blocks into the wave's LDS tile ------
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sb = vsc[i] & 0xFFFFu;
+      const h2 d2 = as_h2(sb | (sb << 16));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t cw = w == 0 ? vc[i].x : w == 1 ? vc[i].y : w == 2 ? vc[i].z : vc[i].w;
+        const uint4 p = dequant8(cw, d2);
+        *reinterpret_cast<uint4*>(lds + wrw[w] + 4096 * i) = p;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);            // the next V codes reuse these registers
+    load_v(k + kWaves);
+
+    // ---- scores S^T[16 h + 4 grp + i, 16 rt + c] ----------------------------
+    f4 s[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) s[rt][0] = s[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t sb = j < 4 ? (ksc[h] & 0xFFFFu) : (ksc[h] >> 16);
+        const uint4 a = dequant8(word(kc[h], j), as_h2(sb | (sb << 16)));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          s[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), bq(rt, j), s[rt][h], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(k + kWaves);
+
+    // ---- V^T operands of the first value products (read ahead) -------------
+    auto load_a = [&](int dt) {
+      const int base = rdl[dt & 7] + 256 * (dt >> 3);
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + base));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + base + 16 * kVRow));
+      return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    h8 av[4];
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) av[dt] = load_a(dt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- softmax (base 2), lazy running max ---------------------------------
+    float sv[RT][8];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) sv[rt][v] = s[rt][v >> 2][v & 3] * c2;
+    if (t0 + kTileKeys - 1 > T - M) {              // the tile reaches past some row's limit
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int t = t0 + 16 * (v >> 2) + 4 * grp + (v & 3);
+          if (t > lim[rt]) sv[rt][v] = -__builtin_inff();
+        }
+    }
+    bool grow = false;
+    float mx[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      mx[rt] = sv[rt][0];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) mx[rt] = fmaxf(mx[rt], sv[rt][v]);
+      grow = grow || mx[rt] > m_run[rt] + kRescaleGap;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float m_new = fmaxf(m_run[rt], halves_max(rows16_max(mx[rt])));
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) o[rt][dt] *= alpha;
+        l_run[rt] *= alpha;
+        m_run[rt] = m_new;
+      }
+    }
+    uint4 pb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float p[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(sv[rt][v] - m_run[rt]);
+        l_run[rt] += p[v];
+      }
+      uint32_t pk[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2 t2 = {(_Float16)p[2 * i], (_Float16)p[2 * i + 1]};
+        pk[i] = as_u32(t2);
+      }
+      pb[rt] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- O^T[d, r] += V^T[d, t] P^T[t, r] -----------------------------------
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      if (dt + 3 < 16) av[(dt + 3) & 3] = load_a(dt + 3);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[dt & 3], as_h8(pb[rt]), o[rt][dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  int k = wave;                                 // this wave's tiles: k, k + 8, ... of the slice
+  if (exists(k)) {
+    load_k(k);
+    load_v(k);
+  }
+#pragma unroll 1
+  for (; exists(k); k += kWaves) process(k);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) l_run[rt] = halves_sum(rows16_sum(l_run[rt]));   // the row's 4 lanes
+
+  // ---- combine the 8 waves in LDS (the V tiles are free now) ----------------
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);             // [wave][rt][dt][lane] float4s
+  float* mxs = red + 4 * RT * 16 * 64 * 4;                // [wave][32 rows]
+  float* lsum = mxs + kWaves * 32;                        // [wave][32 rows]
+  if (grp == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mxs[wave * 32 + 16 * rt + c] = m_run[rt];
+  }
+  __syncthreads();
+  float m_all[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_all[rt] = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) m_all[rt] = fmaxf(m_all[rt], mxs[w * 32 + 16 * rt + c]);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_all[rt]);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) o[rt][dt] *= alpha;
+    l_run[rt] *= alpha;
+  }
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    __syncthreads();
+    if (wave >= half && wave < 2 * half) {
+      float4* dst = reinterpret_cast<float4*>(red) + (size_t)(wave - half) * RT * 16 * 64;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt)
+          dst[(rt * 16 + dt) * 64 + lane] = make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+      if (grp == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) lsum[(wave - half) * 32 + 16 * rt + c] = l_run[rt];
+      }
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float4* src = reinterpret_cast<const float4*>(red) + (size_t)wave * RT * 16 * 64;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+          const float4 f = src[(rt * 16 + dt) * 64 + lane];
+          o[rt][dt][0] += f.x;
+          o[rt][dt][1] += f.y;
+          o[rt][dt][2] += f.z;
+          o[rt][dt][3] += f.w;
+        }
+        l_run[rt] += lsum[wave * 32 + 16 * rt + c];
+      }
+    }
+  }
+
+  // ---- wave 0 writes this slice's partial (rows < R) -------------------------
+  // D row 4 grp + i of product dt is position 16 dt + 4 grp + i of the V tile
+  // row: channel 16 dt + 8 (grp / 2) + 2 (grp % 2) + (0, 4, 1, 5)[i].
+  if (wave == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = 16 * rt + c;
+      if (r < R) {
+        const size_t row = ((size_t)split * Hkv + head) * R + r;
+        float* po = part_o + row * kD + 8 * (grp >> 1) + 2 * (grp & 1);
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+          *reinterpret_cast<float2*>(po + 16 * dt) = make_float2(o[rt][dt][0], o[rt][dt][2]);
+          *reinterpret_cast<float2*>(po + 16 * dt + 4) = make_float2(o[rt][dt][1], o[rt][dt][3]);
+        }
+        if (grp == 0) {
+          part_ml[2 * row] = m_all[rt];
+          part_ml[2 * row + 1] = l_run[rt];
+        }
+      }
+    }
+  }
+}
+
 // ---- kernel 2: merge the slices -------------------------------------------
 // grid (H_kv * R, D / 64), 256 threads: thread (ss, dd) takes channel
 // 64 blockIdx.y + dd of slices ss, ss + 4, ... with its own running max (one
@@ -542,8 +933,15 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const u
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             ((rows * kD * sizeof(float) + 255) & ~(size_t)255));
-  hipLaunchKernelGGL(attn_partial_kernel, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
-                     v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
+  // R = M * G query rows per K/V head: up to 16 on the 16-row form (16 x 16 x 32
+  // products), else the 32-row form.
+  const int R = M * (Hq / Hkv);
+  if (R <= 16)
+    hipLaunchKernelGGL(attn16_partial_kernel<1>, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
+                       v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
+  else
+    hipLaunchKernelGGL(attn_partial_kernel, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
+                       v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(Hkv * M * (Hq / Hkv), kD / 64), dim3(256), 0, s, part_o, part_ml,
