@@ -10,31 +10,39 @@
 // over the cache positions t <= T - M + m.  K and V are token-major rows of
 // H_kv * D values in the weights' 32-element 4-bit block format.
 //
-// gfx950 design (bound by streaming the cache from HBM).  Two forms of the
-// first kernel: up to R = 16 query rows per K/V head (one query token at
-// G = 5, up to three) the 16-row form below (attn16_partial_kernel, 16 x 16
-// x 32 products), above that the 32-row form described here:
+// gfx950 design (bound by streaming the cache from HBM):
 //  * One workgroup (8 waves) per (K/V head g, slice of the keys); a wave
 //    takes 32-key tiles of its slice in turn and keeps its own running max,
 //    sum and output (flash-decoding).  The R = M * G query rows of head g
-//    are the 32 columns of every matrix product (rows past R are zero).
-//  * Scores: S^T[t, r] = K[t, :] . Q[r, :] on v_mfma_f32_32x32x16_f16.  A
-//    lane loads its key's 64 bytes of codes (half a head row) and the 4
-//    block scales, and dequantizes one code word per product into fp16
+//    are the columns of every matrix product, in RT tiles of 16 (RT = 1 up
+//    to R = 16, i.e. up to three query tokens at G = 5; RT = 2 up to 32).
+//  * All products are v_mfma_f32_16x16x32_f16; lane l has c = l % 16 and
+//    slot group grp = l / 16.  Scores S^T[t, r]: A = K rows (key 16 h + c of
+//    the tile's half h), B = Q^T (column r = 16 rt + c); D rows
+//    4 grp .. 4 grp + 3.  Lane (c, grp) loads bytes [32 grp, 32 grp + 32) of
+//    its key's 128 code bytes (blocks 2 grp and 2 grp + 1) and their two
+//    scales, and dequantizes one code word per product into fp16
 //    (magic-exponent nibble unpack, exact integer codes, one rounding of
-//    q * d); Q^T sits in LDS in the matching d order.  A lane then holds 16
-//    keys of one query row: the row max and sum need one cross-half swap.
+//    q * d): product j takes channels 64 grp + 8 j .. + 7, and Q^T (in LDS)
+//    holds the same channels in the unpack's pair order.
 //  * Softmax in base 2, in fp32, with a lazy running max: the output is
-//    rescaled only when some row's max grows by more than 8 (p <= 256).
-//  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  The V codes are loaded 8
-//    lanes per key row (one 16-byte block each, so a load instruction covers
-//    8 whole cache lines) and dequantized into a wave-private LDS tile
-//    (512-byte rows, 16-byte chunks XOR-swizzled by key so that neither the
-//    row writes nor the column reads meet bank conflicts); the product's
-//    V^T operand comes out
-//    of that tile with the transposing LDS read (ds_read_b64_tr_b16: four
-//    keys of one channel per lane per read); P^T comes from the scores'
-//    registers through two v_permlane32_swap per 16 keys.
+//    rescaled (and the row max taken across the row's four lanes) only when
+//    some score passes its row's max by more than 8 (p <= 256).
+//  * Values: O^T[d, r] += V^T[d, t] P^T[t, r].  Slot 8 grp + 4 h + i of a
+//    value product is key 16 h + 4 grp + i, so P^T, the B operand, is the
+//    lane's own 8 probabilities.  The V codes are loaded 8 lanes per key row
+//    (one 16-byte block each, so a load instruction covers 8 whole cache
+//    lines) and dequantized into a wave-private LDS tile (512-byte rows); the
+//    V^T operand comes out of it through two transposing reads per product
+//    (ds_read_b64_tr_b16: keys 4 grp + 0..3 and 16 + 4 grp + 0..3 of one
+//    channel).  16-byte chunk n of row t sits at n ^ f(t), f linear over the
+//    bits of t % 8 (bit 0 -> 2, bit 1 -> 5, bit 2 -> 9), so that the row
+//    writes (8 keys x 2 blocks per 16 lanes) and the transposing reads
+//    (8 keys x 2 chunks per 32 lanes) meet no bank conflicts with 32 or 64
+//    banks.
+//  * A tile is read through buffer resources that start at the tile and end
+//    at the cache's end (no bytes for a tile that does not exist), so each
+//    lane's load offsets are fixed and keys past T read zeros.
 //  * The 8 waves' partial results are combined in LDS, each workgroup writes
 //    one partial (rows < R only), and a second kernel merges the slices.
 
@@ -50,24 +58,16 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVRow = 512;                // bytes per dequantized V row in LDS
 constexpr int kVTile = kTileKeys * kVRow; // bytes per wave's V tile
-constexpr int kQtBytes = 16 * 64 * 16;    // Q^T operands in LDS
 constexpr float kNegBig = -1.0e30f;       // running-max start (finite: no inf - inf)
 constexpr float kRescaleGap = 8.0f;       // base-2 growth of the max that forces a rescale
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kMergeBatch = 16;           // slice loads in flight per thread in the merge
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-// LDS: Q^T B operands [product c][lane] (uint4), then one dequantized V tile
-// per wave, [key][512 bytes].  After the key loop the whole area serves the
-// combine of the 8 waves.
-constexpr int kLdsBytes = kQtBytes + kWaves * kVTile;
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
@@ -97,383 +97,15 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// lanes 32..63 of a <-> lanes 0..31 of b
-__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-
 // ---- kernel 1: one partial result per (K/V head, key slice) ---------------
 // grid (S, H_kv), 8 waves.  Slice s covers the key tiles s + k S, k < tps:
 // the slices interleave, so at any time all workgroups read neighbouring
 // tiles (the whole chip sweeps the cache as one window, which streams faster
 // than S separate regions).
 // part_o: [S][H_kv][R][D] fp32, part_ml: [S][H_kv][R][2] (base-2 max, sum).
-__global__ void __launch_bounds__(kThreads)
-attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
-                    const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
-                    const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
-                    float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
-  __shared__ __align__(16) unsigned char lds[kLdsBytes];
-  uint4* qt = reinterpret_cast<uint4*>(lds);
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int r = lane & 31;                 // query row of this lane (a matrix column)
-  const int hh = lane >> 5;                // half: keys 4hh.. of each group of 8, d half
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int G = Hq / Hkv;
-  const int R = M * G;
-  const int ntiles = (T + kTileKeys - 1) / kTileKeys;
-  const int S = gridDim.x;
-  // physical tile of this slice's k-th tile, and whether it exists
-  auto phys = [&](int k) { return k * S + split; };
-  auto exists = [&](int k) { return k < tps && phys(k) < ntiles; };
 
-  // ---- Q^T into LDS: entry (c, lane') holds Q[r', 128 h' + 8 c + (0,4,1,5,2,6,3,7)]
-  for (int e = tid; e < 16 * 64; e += kThreads) {
-    const int c = e >> 6, l2 = e & 63;
-    const int r2 = l2 & 31, h2i = l2 >> 5;
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (r2 < R) {
-      const int m = r2 / G, hq = g * G + r2 % G;
-      const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)m * Hq + hq) * kD + 128 * h2i + 8 * c);
-      o.x = (w.x & 0xFFFFu) | (w.z << 16);          // (e0, e4)
-      o.y = (w.x >> 16) | (w.z & 0xFFFF0000u);      // (e1, e5)
-      o.z = (w.y & 0xFFFFu) | (w.w << 16);          // (e2, e6)
-      o.w = (w.y >> 16) | (w.w & 0xFFFF0000u);      // (e3, e7)
-    }
-    qt[e] = o;
-  }
-  __syncthreads();
-
-  // ---- cache rows: key t's codes for head g are bytes [g*128, g*128+128) of its row
-  const int row_codes = Hkv * kD / 2;           // bytes per cache row
-  const int row_scales = Hkv * kD / kBlock;     // fp16 per cache row
-  const __amdgpu_buffer_rsrc_t rkc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)k_codes, 0, T * row_codes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rvc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)v_codes, 0, T * row_codes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)k_scales, 0, T * row_scales * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)v_scales, 0, T * row_scales * 2, kRsrcWord3);
-  const uint32_t lane_codes = (uint32_t)(g * (kD / 2) + 64 * hh);      // + key * row_codes
-  const uint32_t lane_scales = (uint32_t)((g * (kD / kBlock) + 4 * hh) * 2);
-  const uint32_t vlane_codes = (uint32_t)(g * (kD / 2) + kBlockBytes * (lane >> 3));   // V: block l >> 3
-  const uint32_t vlane_scales = (uint32_t)((g * (kD / kBlock) + (lane >> 3)) * 2);
-
-  // K: this lane's 64 code bytes and 4 block scales (fp16 x 4); the next
-  // tile's are requested as soon as this tile's scores are issued.  V: load i
-  // gives this lane the 16 code bytes (one block) of key 8 i + (l & 7), block
-  // l >> 3, and that block's scale, so each load covers 8 whole 128-byte
-  // lines (in the operand layout of K a load touches 32); the next tile's are
-  // requested as soon as this one sits in LDS.
-  uint4 kc[4], vc[4];
-  v2u ksc;
-  uint32_t vsc[4];
-  auto load_k = [&](int k, uint4 (&kc)[4], v2u& ksc) {
-    const int key = phys(k) * kTileKeys + r;
-    const bool live = exists(k) && key < T;
-    const uint32_t oc = live ? (uint32_t)key * row_codes + lane_codes : kOutOfRange;
-    const uint32_t os = live ? (uint32_t)key * row_scales * 2 + lane_scales : kOutOfRange;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rkc, oc, 16 * i, 0);
-      kc[i] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-    ksc = __builtin_amdgcn_raw_buffer_load_b64(rks, os, 0, 0);
-  };
-  auto load_v = [&](int k) {
-    const bool tile_live = exists(k);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = phys(k) * kTileKeys + 8 * i + (lane & 7);
-      const bool live = tile_live && key < T;
-      const uint32_t oc = live ? (uint32_t)key * row_codes + vlane_codes : kOutOfRange;
-      const uint32_t os = live ? (uint32_t)key * row_scales * 2 + vlane_scales : kOutOfRange;
-      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rvc, oc, 0, 0);
-      vc[i] = make_uint4(v[0], v[1], v[2], v[3]);
-      vsc[i] = __builtin_amdgcn_raw_buffer_load_b16(rvs, os, 0, 0);
-    }
-  };
-  auto scale2 = [](v2u s, int b) {          // block b (0..3) of the lane's 4 scales, as a pair
-    const uint32_t w = b < 2 ? s[0] : s[1];
-    const uint32_t h = (b & 1) ? (w >> 16) : (w & 0xFFFFu);
-    return as_h2(h | (h << 16));
-  };
-  auto word = [](const uint4 (&c)[4], int i) {
-    const uint4 v = c[i >> 2];
-    const int j = i & 3;
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-  };
-
-  // the last position query row r may see (rows past R: every key)
-  const int lim = r < R ? T - M + r / G : T - 1;
-  const float c2 = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(D)
-
-  f16v o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
-
-  // ---- the wave's V tile: key t's row holds its 256 channels as fp16 in
-  // the dequantized pair order (column 8 i + (0, 2, 4, 6, 1, 3, 5, 7)[e] is
-  // channel 8 i + e); 16-byte chunk n of row t sits at chunk n ^ sw(t), with
-  // sw linear over the bits of t % 16: bit 0 -> 4, bit 1 -> 10, bit 2 -> 1,
-  // bit 3 -> 8.  Taken over 32 banks with 16 lanes per cycle, or over 64
-  // banks with 32 lanes per cycle (the conflict counter fits both), every
-  // transposed read (4 keys x 2 or 4 chunks) and every row write (8 or 16
-  // keys of one chunk) then touches distinct banks.
-  const int vt = kQtBytes + wave * kVTile;
-  // row writes: V load i of this lane (key t = 8 i + u, u = l & 7, block p =
-  // l >> 3) fills logical chunks 4 p + w (w = 0..3) of row t; sw(t) is
-  // sw(u) ^ 8 (i & 1), so the address is (wr[i & 1] + 4096 i) ^ 16 w.
-  int wr[2];
-  {
-    const int u = lane & 7, p = lane >> 3;
-    const int su = (4 * (u & 1)) ^ (10 * ((u >> 1) & 1)) ^ ((u >> 2) & 1);
-#pragma unroll
-    for (int ip = 0; ip < 2; ++ip)
-      wr[ip] = vt + u * kVRow + 16 * ((4 * p) ^ ((su ^ (8 * ip)) & 12)) + 16 * (su & 3);
-  }
-  // transposed reads (A operand of the 32 x 32 x 16 product): lane l takes
-  // column 32 dt + l % 32 of keys 16 cp + 8 (l / 32) + 4 j + (0..3).  Within
-  // each 16-lane group, lane 4 k + i / 4 reads the 8 bytes that the
-  // transpose hands to lane i as its element k: key 4 j + x (x = (l >> 2) & 3),
-  // columns 4 (l & 3) + (0..3) of the group's 16, i.e. logical chunk
-  // 4 dt + 2 grp + b (grp = (l >> 4) & 1, b = (l & 3) >> 1).  The key's
-  // bits are x (0-1), j (2) and l / 32 (3), so that chunk sits at
-  // 16 (dt / 4) + 4 ((dt % 4) ^ y) + 2 (grp ^ (x >> 1)) + (b ^ j) with
-  // y = (x & 1) + 2 ((x >> 1) ^ (l / 32)): the address for dt % 4 = e is
-  // rd[j] + 64 (e ^ y); cp and dt / 4 only add constants (8192 cp + 256 (dt / 4)).
-  const int y64 = 64 * ((((lane >> 2) & 3) & 1) | (((((lane >> 2) & 3) >> 1) ^ (lane >> 5)) << 1));
-  int rd[2];
-  {
-    const int x = (lane >> 2) & 3;
-    const int grp = (lane >> 4) & 1;
-    const int bsel = (lane & 3) >> 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      rd[j] = vt + (8 * (lane >> 5) + 4 * j + x) * kVRow + 32 * (grp ^ (x >> 1)) + 16 * (bsel ^ j) +
-              8 * (lane & 1);
-  }
-  typedef __attribute__((address_space(3))) unsigned char lds_u8;
-  lds_u8* const lds3 = (lds_u8*)lds;
-
-  // one tile; kc holds its K, then the next tile's.  The
-  // scheduling fences keep each LDS operand read three products ahead of its
-  // use (the compiler would otherwise issue it just before the product).
-  auto process = [&](int k) {
-    const int t0 = phys(k) * kTileKeys;
-    // ---- V: dequantize this lane's 4 blocks into the wave's LDS tile ------
-    int wa[2] = {wr[0], wr[1]};
-    asm volatile("" : "+v"(wa[0]), "+v"(wa[1]));  // addresses made per tile, not held in registers
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t sb = vsc[i] & 0xFFFFu;
-      const h2 d2 = as_h2(sb | (sb << 16));
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint4 p = dequant8(word(vc, 4 * i + w), d2);
-        *reinterpret_cast<uint4*>(lds + ((wa[i & 1] + 4096 * i) ^ (16 * w))) = p;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);            // the next V codes reuse these registers
-    load_v(k + kWaves);                           // next tile of this wave (past the end: zeros)
-
-    // ---- scores S^T[t, r] ---------------------------------------------------
-    f16v s = {};
-    uint4 bq[4];
-#pragma unroll
-    for (int c = 0; c < 3; ++c) bq[c] = qt[c * 64 + lane];
-    uint4 a = dequant8(word(kc, 0), scale2(ksc, 0));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      if (c + 3 < 16) bq[(c + 3) & 3] = qt[(c + 3) * 64 + lane];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_h8(a), as_h8(bq[c & 3]), s, 0, 0, 0);
-      if (c + 1 < 16) a = dequant8(word(kc, c + 1), scale2(ksc, (c + 1) >> 2));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    load_k(k + kWaves, kc, ksc);                  // next tile of this wave (past the end: zeros)
-
-    // ---- V^T operands of the first three value products (read ahead) ------
-    int ra[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int b = rd[j];
-      asm volatile("" : "+v"(b));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ra[j][e] = b + (y64 ^ (64 * e));
-    }
-    auto load_a = [&](int idx) {                  // product idx: cp = idx / 8, dt = idx % 8
-      const int dt = idx & 7;
-      const int off = 16 * kVRow * (idx >> 3) + 256 * (dt >> 2);
-      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + ra[0][dt & 3] + off));
-      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(lds3 + ra[1][dt & 3] + off));
-      return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    h8 av[4];
-#pragma unroll
-    for (int idx = 0; idx < 3; ++idx) av[idx] = load_a(idx);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- softmax (base 2), lazy running max -------------------------------
-    float sv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sv[v] = s[v] * c2;
-    if (t0 + kTileKeys - 1 > T - M) {              // the tile reaches past some row's limit
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (t > lim) sv[v] = -__builtin_inff();
-      }
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleGap) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(sv[v] - m_run);
-      l_run += p[v];
-    }
-    // P^T as the B operand of two 16-key products: lane (r, hh) needs keys
-    // 16 c' + 8 hh + 0..7; it holds keys 8 i + 4 hh + 0..3 (i = 0..3).
-    uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const h2 t2 = {(_Float16)p[2 * i], (_Float16)p[2 * i + 1]};
-      pk[i] = as_u32(t2);
-    }
-    swap32(pk[0], pk[2]);
-    swap32(pk[1], pk[3]);
-    swap32(pk[4], pk[6]);
-    swap32(pk[5], pk[7]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- O^T[d, r] += V^T[d, t] P^T[t, r] ---------------------------------
-#pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      if (idx + 3 < 16) av[(idx + 3) & 3] = load_a(idx + 3);
-      const int cp = idx >> 3;
-      const uint4 bb = make_uint4(pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]);
-      o[idx & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[idx & 3], as_h8(bb), o[idx & 7], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  int k = wave;                                 // this wave's tiles: k, k + 8, ... of the slice
-  if (exists(k)) {
-    load_k(k, kc, ksc);
-    load_v(k);
-  }
-#pragma unroll 1
-  for (; exists(k); k += kWaves) process(k);
-  l_run += __shfl_xor(l_run, 32, 64);
-
-  // ---- combine the 8 waves in LDS (the V tiles are free now) ----------------
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);             // [wave][idx][lane] float4s + max
-  float* mxs = red + 4 * 32 * 64 * 4;                     // after 4 waves' outputs: [wave][32]
-  if (hh == 0) mxs[wave * 32 + r] = m_run;
-  __syncthreads();
-  float m_all = kNegBig;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) m_all = fmaxf(m_all, mxs[w * 32 + r]);
-  {
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_all);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-    l_run *= alpha;
-  }
-  float* lsum = mxs + kWaves * 32;                        // [wave][64]
-#pragma unroll
-  for (int half = kWaves / 2; half >= 1; half >>= 1) {
-    __syncthreads();
-    if (wave >= half && wave < 2 * half) {
-      float4* dst = reinterpret_cast<float4*>(red) + (size_t)(wave - half) * 32 * 64;
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        dst[i * 64 + lane] = make_float4(o[i >> 2][4 * (i & 3)], o[i >> 2][4 * (i & 3) + 1],
-                                         o[i >> 2][4 * (i & 3) + 2], o[i >> 2][4 * (i & 3) + 3]);
-      lsum[(wave - half) * 64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float4* src = reinterpret_cast<const float4*>(red) + (size_t)wave * 32 * 64;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float4 f = src[i * 64 + lane];
-        o[i >> 2][4 * (i & 3)] += f.x;
-        o[i >> 2][4 * (i & 3) + 1] += f.y;
-        o[i >> 2][4 * (i & 3) + 2] += f.z;
-        o[i >> 2][4 * (i & 3) + 3] += f.w;
-      }
-      l_run += lsum[wave * 64 + lane];
-    }
-  }
-
-  // ---- wave 0 writes this slice's partial (rows < R) -------------------------
-  if (wave == 0 && r < R) {
-    const size_t row = ((size_t)split * Hkv + g) * R + r;
-    float* po = part_o + row * kD;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {   // rows 8 i + 4 hh + (0..3): channels 8 i + (0, 4, 1, 5) + 2 hh
-        float* pd = po + 32 * dt + 8 * i + 2 * hh;
-        *reinterpret_cast<float2*>(pd) = make_float2(o[dt][4 * i], o[dt][4 * i + 2]);
-        *reinterpret_cast<float2*>(pd + 4) = make_float2(o[dt][4 * i + 1], o[dt][4 * i + 3]);
-      }
-    if (hh == 0) {
-      part_ml[2 * row] = m_all;
-      part_ml[2 * row + 1] = l_run;
-    }
-  }
-}
-
-// ---- kernel 1, 16-row form: R <= 16 (RT = 1) or 32 (RT = 2) -----------------
-// The same partial result on v_mfma_f32_16x16x32_f16, with the query rows in
-// RT tiles of 16 columns, so that R <= 16 (one query token at G = 5 up to
-// three) pays for 16 columns instead of 32.  Lane l: c = l % 16, grp = l / 16.
-//  * Scores S^T[t, r]: A = K rows (key 16 h + c of the tile's half h, slots
-//    8 grp ..), B = Q^T (column r = 16 rt + c), D rows 4 grp .. 4 grp + 3.
-//    Lane (c, grp) loads bytes [32 grp, 32 grp + 32) of its key's 128 (blocks
-//    2 grp and 2 grp + 1, so 4 lanes share each 128-byte line of a load
-//    instruction) and their two scales; product j takes code word j, that is
-//    channels 64 grp + 8 j .. 64 grp + 8 j + 7 in the dequantized pair order,
-//    and Q^T holds the same channels.
-//  * A lane ends with 4 keys x 2 halves of its query row: slot 8 grp + 4 h + i
-//    of the value product is key 16 h + 4 grp + i, so P^T, the B operand of
-//    O^T[d, r] += V^T[d, t] P^T[t, r], is the lane's own 8 probabilities.
-//  * V^T comes from the wave's LDS tile through two transposing reads per
-//    product (keys 4 grp + 0..3 and 16 + 4 grp + 0..3 of one channel).  Rows
-//    are 512 bytes; 16-byte chunk n of row t sits at n ^ f(t), f linear over
-//    the bits of t % 8 (bit 0 -> 2, bit 1 -> 5, bit 2 -> 9): the row writes
-//    (8 keys x 2 blocks per 16 lanes) and the transposing reads (8 keys x 2
-//    chunks per 32 lanes) then meet no bank conflicts, with 32 or 64 banks.
-//  * Lazy running max as in the 32-row form: the row max across a row's four
-//    lanes is taken only when some score passes its row's max by more than 8.
-__device__ __forceinline__ int vt_swizzle(int t) {   // f(t) on t % 8
+// f(t): the V tile's chunk swizzle of row t (linear over the bits of t % 8)
+__device__ __forceinline__ int vt_swizzle(int t) {
   return (2 * (t & 1)) ^ (5 * ((t >> 1) & 1)) ^ (9 * ((t >> 2) & 1));
 }
 
@@ -493,15 +125,18 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 template <int RT>
 __global__ void __launch_bounds__(kThreads)
-attn16_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
-                      const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
-                      const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
-                      float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
+attn_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+                    const uint16_t* __restrict__ k_scales, const uint8_t* __restrict__ v_codes,
+                    const uint16_t* __restrict__ v_scales, float* __restrict__ part_o,
+                    float* __restrict__ part_ml, int M, int Hq, int Hkv, int T, int tps) {
   static_assert(RT == 1 || RT == 2, "16 or 32 query rows");
-  constexpr int kQtEntries = RT * 8 * 64;                 // [rt][product j][lane] uint4
-  constexpr int kQt16Bytes = kQtEntries * 16;
-  constexpr int kLds16 = kQt16Bytes + kWaves * kVTile;
-  __shared__ __align__(16) unsigned char lds[kLds16];
+  // LDS: Q^T B operands [rt][product j][lane] (uint4), then one dequantized V
+  // tile per wave, [key][512 bytes].  After the key loop the whole area
+  // serves the combine of the 8 waves.
+  constexpr int kQtEntries = RT * 8 * 64;
+  constexpr int kQtBytes = kQtEntries * 16;
+  constexpr int kLdsBytes = kQtBytes + kWaves * kVTile;
+  __shared__ __align__(16) unsigned char lds[kLdsBytes];
   uint4* qt = reinterpret_cast<uint4*>(lds);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -627,7 +262,7 @@ attn16_partial_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict_
   // reads: lane (c, grp) addresses row 4 grp + c / 4 (+ 16 for the second
   // read), chunk 2 dt + (c % 4) / 2, half c % 2, which is
   // (rd ^ 32 (dt % 8)) + 256 (dt / 8) (+ 8192).
-  const int vt = kQt16Bytes + wave * kVTile;
+  const int vt = kQtBytes + wave * kVTile;
   const int wr = vt + (lane & 7) * kVRow + 16 * ((4 * (lane >> 3)) ^ vt_swizzle(lane & 7));
   const int trow = 4 * grp + (c >> 2);
   const int rd = vt + trow * kVRow + 16 * (((c & 3) >> 1) ^ vt_swizzle(trow)) + 8 * (c & 1);
@@ -933,14 +568,13 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint8_t* k_codes, const u
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                             ((rows * kD * sizeof(float) + 255) & ~(size_t)255));
-  // R = M * G query rows per K/V head: up to 16 on the 16-row form (16 x 16 x 32
-  // products), else the 32-row form.
+  // R = M * G query rows per K/V head: one 16-row tile up to 16, else two.
   const int R = M * (Hq / Hkv);
   if (R <= 16)
-    hipLaunchKernelGGL(attn16_partial_kernel<1>, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
+    hipLaunchKernelGGL(attn_partial_kernel<1>, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
                        v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
   else
-    hipLaunchKernelGGL(attn_partial_kernel, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
+    hipLaunchKernelGGL(attn_partial_kernel<2>, dim3(S, Hkv), dim3(kThreads), 0, s, q, k_codes, k_scales, v_codes,
                        v_scales, part_o, part_ml, M, Hq, Hkv, (int)T, tps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
