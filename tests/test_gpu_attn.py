@@ -36,10 +36,14 @@ def _run(torch, q, kc, ks, vc, vs, hkv):
 
 
 # (M, H_q, H_kv, T): the reading's geometry at M = 1..5 with ragged and short
-# caches; MQA (one K/V head); R = M * G = 32 (the widest); T = M.
+# caches; MQA (one K/V head); R = M * G = 32 (the widest); T = M.  The query
+# rows of a K/V head run in tiles of 16: R = 16 fills one tile, R = 17 puts a
+# single row in a second.  T = 40,001 gives 64 key slices of 20 tiles with a
+# one-key last tile.
 SHAPES = [
     (1, 20, 4, 100), (5, 20, 4, 300), (4, 20, 4, 1000), (2, 20, 4, 33), (3, 20, 4, 3),
     (4, 8, 2, 777), (3, 4, 1, 65), (1, 32, 1, 4096), (1, 1, 1, 1), (6, 10, 2, 5000),
+    (1, 17, 1, 500), (3, 20, 4, 40001),
 ]
 
 
