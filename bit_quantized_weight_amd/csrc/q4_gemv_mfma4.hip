@@ -47,6 +47,17 @@ constexpr int kSplitSliceSteps = 4;        // longest slice of a split row
 // Deepest copy with two row groups: with two A operands (M > 4) the 8- and
 // 10-step copies would spill registers.
 __host__ __device__ constexpr int max_pair_steps(int M) { return M > 4 ? 6 : kMaxSliceSteps; }
+// Activation entries per block in LDS, and the slot of row m in block b.
+// Up to M = 4 the rows sit in order (a stride of M entries per block).  With
+// two A operands (M = 5..7) a stride of M would make the 64 lanes of an
+// operand read (lane 4 blk + c reads row c of block blk) collide on banks,
+// so each block takes 8 entries and row m sits at slot (m + 4 (b0 ^ b1)) % 8,
+// b0 and b1 the low bits of b: every operand read then touches distinct
+// banks (checked for 32 and 64 banks).
+__host__ __device__ constexpr int row_stride(int M) { return M > 4 ? 8 : M; }
+__host__ __device__ constexpr int row_slot(int M, int m, int b) {
+  return M > 4 ? (m + 4 * ((b ^ (b >> 1)) & 1)) & 7 : m;
+}
 constexpr int kWideTileMinWgs = 512;       // 64-row tiles only with this many workgroups
 constexpr int kMinWgs = 256;               // one workgroup per CU
 constexpr int kCachePolicyNT = 2;          // non-temporal: codes are read once, in whole lines
@@ -168,7 +179,8 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
   // (m fastest, then b: the 64 lanes of an operand read, lane 4 blk + c, touch
   // one contiguous run of 16-byte entries, so the LDS reads are conflict-free)
   uint4* xs = smem;
-  float* bias = reinterpret_cast<float*>(smem + bpad * M * 4);
+  constexpr int MS = row_stride(M);
+  float* bias = reinterpret_cast<float*>(smem + bpad * MS * 4);
   const uint32_t k1032 = 0x64086408u;   // fp16 pair (1032, 1032)
   const uint32_t k72 = 0x54805480u;     // fp16 pair (72, 72)
 #pragma unroll
@@ -187,7 +199,7 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
         o.y = (w0 >> 16) | (w2 & 0xFFFF0000u);   // (e1, e5)
         o.z = (w1 & 0xFFFFu) | (w3 << 16);       // (e2, e6)
         o.w = (w1 >> 16) | (w3 & 0xFFFF0000u);   // (e3, e7)
-        xs[(q * bpad + b) * M + m] = o;
+        xs[(q * bpad + b) * MS + row_slot(M, m, b)] = o;
         s = dot2(o.x, k1032, s);
         s = dot2(o.y, k72, s);
         s = dot2(o.z, k1032, s);
@@ -198,10 +210,11 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
   }
   __syncthreads();
 
-  // A rows past M read row 0 (their products land in D rows that are dropped).
-  const uint4* xa[kASets];                           // + word q: q * bpad * M; + step t: t * kStepBlocks * M
+  // A rows past M read row 4 j, the set's first (their products land in D
+  // rows that are dropped); a step adds 16 blocks, which keeps b0 and b1.
+  const uint4* xa[kASets];                           // + word q: q * bpad * MS; + step t: t * kStepBlocks * MS
 #pragma unroll
-  for (int j = 0; j < kASets; ++j) xa[j] = xs + blk * M + (4 * j + c < M ? 4 * j + c : 0);
+  for (int j = 0; j < kASets; ++j) xa[j] = xs + blk * MS + row_slot(M, 4 * j + c < M ? 4 * j + c : 4 * j, blk);
   const float* ba = bias + blk * MP;                 // + step t: t * kStepBlocks * MP
 
   float yacc[kRowGroups][M];
@@ -224,7 +237,7 @@ mfma4_skinny_kernel(const uint16_t* __restrict__ x, const uint4* __restrict__ co
       for (int q = 0; q < 4; ++q) {
         uint4 a[kASets];
 #pragma unroll
-        for (int j = 0; j < kASets; ++j) a[j] = xa[j][t * kStepBlocks * M + q * bpad * M];
+        for (int j = 0; j < kASets; ++j) a[j] = xa[j][t * kStepBlocks * MS + q * bpad * MS];
 #pragma unroll
         for (int r = 0; r < kRowGroups; ++r) {
           const uint32_t w = word(cw[t][r], q);
@@ -293,7 +306,7 @@ template <int M, int P, int R>
 hipError_t launch_p(const uint16_t* x, const uint8_t* codes, const uint16_t* scales, uint16_t* y,
                     int64_t N, int64_t K, const SkinnyPlan& p, void* ws, hipStream_t s) {
   const int bpad = ((p.blocks_per_split + kStepBlocks - 1) / kStepBlocks) * kStepBlocks;
-  const size_t lds = (size_t)bpad * (M * 4 * sizeof(uint4) + 4 * ((M + 3) / 4) * sizeof(float));
+  const size_t lds = (size_t)bpad * (row_stride(M) * 4 * sizeof(uint4) + 4 * ((M + 3) / 4) * sizeof(float));
   uint32_t* counters = nullptr;
   float* partial = nullptr;
   if (p.splits > 1) {
