@@ -25,6 +25,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 31;  // kernels index rows and columns
 // The skinny kernel addresses one workgroup's rows (<= 64 x K/2 bytes) through
 // a buffer resource with a 32-bit byte range.
 constexpr int64_t kMaxSkinnyK = int64_t(1) << 24;
+// The A8 GEMM addresses a 128-row activation tile ([4][K/32][64] x 16 B) and
+// its chunk offsets with 32-bit buffer sizes and offsets, which stay below
+// 2^31 only for K < 2^24.
+constexpr int64_t kMaxA8K = (int64_t(1) << 24) - 64;
 
 constexpr int kMaxBatch = 1 << 20;
 
@@ -188,7 +192,7 @@ static int a8_common(const uint16_t* x, const uint8_t* codes, const uint16_t* sc
                      int64_t K, void* ws, size_t ws_bytes) {
   if (M < 0 || N < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
   if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (M >= kMaxDim || N >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || N >= kMaxDim || K > kMaxA8K) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (M == 0 || N == 0) return 1;  // nothing to do
   if (!out) return Q4W_ERR_INVALID_ARG;
   if (!aligned(out, out_align)) return Q4W_ERR_MISALIGNED;
@@ -217,7 +221,7 @@ int a8w4_prepare_act(const uint16_t* x, int64_t M, int64_t K, void* ws, size_t w
                      hipStream_t stream) {
   if (M < 0 || K < 0) return Q4W_ERR_INVALID_ARG;
   if (K % q4w::kActGroup != 0) return Q4W_ERR_UNSUPPORTED_SHAPE;
-  if (M >= kMaxDim || K > kMaxSkinnyK) return Q4W_ERR_UNSUPPORTED_SHAPE;
+  if (M >= kMaxDim || K > kMaxA8K) return Q4W_ERR_UNSUPPORTED_SHAPE;
   if (M == 0 || K == 0) return Q4W_OK;
   if (!x) return Q4W_ERR_INVALID_ARG;
   if (!aligned(x, 16)) return Q4W_ERR_MISALIGNED;

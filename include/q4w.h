@@ -148,7 +148,8 @@ int a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
  *   and write y[m, n] = fp16_RNE(sum_b sa[m, b/2] * d[n, b] * I[m, n, b])
  *   with the rescale in fp32.
  *   x [M, K] fp16 16-byte aligned; y [M, N] fp16 4-byte aligned.
- *   K % 64 == 0 and K <= 2^24 (else UNSUPPORTED_SHAPE); any M, N >= 1.
+ *   K % 64 == 0 and K < 2^24 (else UNSUPPORTED_SHAPE: the GEMM's 32-bit buffer
+ *   ranges over a 128-row activation tile reach 2^31 at K = 2^24); any M, N >= 1.
  *   ws: at least a8w4_ws_bytes(M, K) bytes, 256-byte aligned.  It holds the
  *   quantized activations and, once M rounded up to 128 reaches 256 rows, a
  *   64 MiB region (arrival counters, then fp32 partial tiles) that the GEMM

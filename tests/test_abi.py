@@ -247,6 +247,16 @@ def test_a8_checks(L):
     assert gp(p(A), p(A), NUL, p(A), 64, 32, 128, ws, NUL) == INVALID
     dbg = L.a8w4_debug_block_acc
     assert dbg(p(A), p(A), p(A), 64, 32, 96, p(A), ws, NUL) == SHAPE
+    # K = 2^24 would take the 128-row tile's 32-bit buffer range to 2^31: refused
+    # by every A8 entry point; 2^24 - 64 passes the shape rules (and then needs
+    # its workspace)
+    big = 1 << 24
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, big, p(A), ws, NUL) == SHAPE
+    assert pr(p(A), 64, big, p(A), ws, NUL) == SHAPE
+    assert gp(p(A), p(A), p(A), p(A), 64, 32, big, ws, NUL) == SHAPE
+    assert dbg(p(A), p(A), p(A), 64, 32, big, p(A), ws, NUL) == SHAPE
+    assert gm(p(A), p(A), p(A), p(A), 64, 32, big - 64, p(A), ws, NUL) == WS
+    assert pr(p(A), 64, big - 64, p(A), ws, NUL) == WS
     assert dbg(p(A), p(A), p(A), 64, 32, 128, NUL, 0, NUL) == WS
     assert dbg(p(A), NUL, p(A), 64, 32, 128, p(A), ws, NUL) == INVALID
 
