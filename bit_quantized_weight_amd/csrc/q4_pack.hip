@@ -62,12 +62,19 @@ __global__ void __launch_bounds__(256) pack_kernel(const float4* __restrict__ w,
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,
                        hipStream_t s) {
   const int64_t nblocks = N * (K / kBlock);
-  const int64_t threads = nblocks * 8;
-  const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     reinterpret_cast<const float4*>(w), nblocks,
-                     reinterpret_cast<uint32_t*>(codes), scales);
-  return hipGetLastError();
+  // Blocks are independent, so a large matrix is packed in pieces of at most
+  // 2^26 blocks: a launch's work-item count (8 per block) stays below 2^32.
+  constexpr int64_t kPiece = int64_t(1) << 26;
+  for (int64_t b0 = 0; b0 < nblocks; b0 += kPiece) {
+    const int64_t nb = nblocks - b0 < kPiece ? nblocks - b0 : kPiece;
+    const int64_t grid = (nb * 8 + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(w + b0 * kBlock), nb,
+                       reinterpret_cast<uint32_t*>(codes + b0 * (kBlock / 2)), scales + b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace q4w

@@ -52,3 +52,24 @@ def test_pack_empty():
     torch = torch_cuda()
     codes, scales = pack(torch.zeros((0, 64), dtype=torch.float32, device="cuda"))
     assert codes.shape == (0, 32) and scales.shape == (0, 2)
+
+
+def test_pack_in_pieces():
+    """More than 2^26 blocks (N = 65600, K = 32768: 67,174,400 blocks, 8.6 GB of
+    fp32 input) are packed in two launches that split at block 2^26, the first
+    block of row 65536; rows on both sides of the split and the last row match
+    the oracle byte for byte."""
+    torch = torch_cuda()
+    n, k = 65600, 32768
+    w = synthetic.weights_device(n, k, 31)
+    codes, scales = pack(w)
+    torch.cuda.synchronize()
+    rows = [0, 65535, 65536, 65537, n - 1]
+    sel = torch.as_tensor(rows, device="cuda")
+    wr = w.index_select(0, sel).cpu().numpy()
+    c = codes.index_select(0, sel).cpu().numpy()
+    s = scales.index_select(0, sel).cpu().numpy()
+    del w, codes, scales
+    q, d = q4.quantize(wr)
+    assert np.array_equal(c, q4.pack(q)), "codes differ"
+    assert np.array_equal(s.view(np.uint16), d.view(np.uint16)), "scales differ"
