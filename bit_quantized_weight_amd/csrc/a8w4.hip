@@ -30,6 +30,7 @@
 
 #include "q4w_internal.h"
 #include <hip/hip_fp16.h>
+#include <algorithm>
 #include <cstddef>
 
 namespace q4w {
@@ -647,11 +648,19 @@ size_t a8_ws_bytes(int64_t M, int64_t K) {
 hipError_t launch_act_quant_rowmajor(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* sa,
                                      hipStream_t s) {
   const int G = (int)(K / kActGroup);
-  const int64_t ngroups = M * G;
-  const int64_t grid = (ngroups * 8 + 255) / 256;
-  hipLaunchKernelGGL(act_quant_rowmajor_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, ngroups, G,
-                     (int)K, xq, sa);
-  return hipGetLastError();
+  // Rows are independent: pieces of at most 2^25 groups (2^28 work-items,
+  // 8 per group) keep a launch far below 2^32 work-items.
+  const int64_t rows_per_piece = std::max<int64_t>(1, (int64_t(1) << 25) / G);
+  for (int64_t m0 = 0; m0 < M; m0 += rows_per_piece) {
+    const int64_t rows = std::min(rows_per_piece, M - m0);
+    const int64_t ngroups = rows * G;
+    const int64_t grid = (ngroups * 8 + 255) / 256;
+    hipLaunchKernelGGL(act_quant_rowmajor_kernel, dim3((unsigned)grid), dim3(256), 0, s, x + m0 * K, ngroups,
+                       G, (int)K, xq + m0 * K, sa + m0 * G);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_act_quant_tiled(const uint16_t* x, int64_t M, int64_t K, void* ws, hipStream_t s) {

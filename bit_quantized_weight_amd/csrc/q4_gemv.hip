@@ -454,9 +454,15 @@ hipError_t launch_skinny(const uint16_t* x, const uint8_t* codes, const uint16_t
 }
 
 hipError_t launch_fill_zero_u16(uint16_t* y, int64_t count, hipStream_t s) {
-  const int64_t grid = (count + 255) / 256;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)grid), dim3(256), 0, s, y, count);
-  return hipGetLastError();
+  // pieces of at most 2^28 elements keep a launch far below 2^32 work-items
+  constexpr int64_t kPiece = int64_t(1) << 28;
+  for (int64_t c0 = 0; c0 < count; c0 += kPiece) {
+    const int64_t n = count - c0 < kPiece ? count - c0 : kPiece;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y + c0, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace q4w

@@ -230,3 +230,37 @@ def test_a8_empty_shapes():
                   torch.zeros((32, 0), dtype=torch.float16, device="cuda"))
     torch.cuda.synchronize()
     assert y.shape == (3, 32) and not host(y).any()
+
+
+def test_act_quant_in_pieces():
+    """a8_quantize_act launches rows in pieces of at most 2^25 groups: at
+    K = 5120 (80 groups per row) a piece is 419,430 rows, so 419,500 rows (a
+    4.3 GB input) take two launches.  Rows on both sides of the split and the
+    last row are bit-exact against the oracle."""
+    torch = torch_cuda()
+    m, k = 419_500, 5120
+    x = synthetic.activations_device(m, k, 123)
+    xq, sa = a8_quantize_act(x)
+    torch.cuda.synchronize()
+    rows = [0, 419_429, 419_430, 419_431, m - 1]
+    sel = torch.as_tensor(rows, device="cuda")
+    xr = x.index_select(0, sel).cpu().numpy()
+    xqr = xq.index_select(0, sel).cpu().numpy()
+    sar = sa.index_select(0, sel).cpu().numpy()
+    del x, xq, sa
+    qa, sa_ref = a8.quantize_act(xr)
+    assert np.array_equal(xqr, qa)
+    assert np.array_equal(sar.view(np.uint32), sa_ref.view(np.uint32))
+
+
+def test_a8_zero_k_fill_in_pieces():
+    """K = 0 fills y with zeros in pieces of at most 2^28 elements: y of
+    1024 x 262,208 (268,500,992 elements, first filled with ones) ends all zero."""
+    torch = torch_cuda()
+    m, n = 1024, (1 << 18) + 64
+    y = torch.ones((m, n), dtype=torch.float16, device="cuda")
+    a8w4_gemm(torch.zeros((m, 0), dtype=torch.float16, device="cuda"),
+              torch.zeros((n, 0), dtype=torch.uint8, device="cuda"),
+              torch.zeros((n, 0), dtype=torch.float16, device="cuda"), y=y)
+    torch.cuda.synchronize()
+    assert not bool((y != 0).any())
