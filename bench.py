@@ -451,15 +451,26 @@ def _timed_calls(fn, budget_s):
 
 
 def cpu_baseline(synthetic, budget_s=4.0):
-    """The oracle, untuned, on the host: the headline GEMV with all BLAS
-    threads and with one, the verify down-projection at M = 5, and the exact
-    A8 route on a token sample of the M = 2048 projection."""
+    """The oracle, untuned, on the host, each workload with all BLAS threads
+    and with one: the headline GEMV, the verify down-projection at M = 5 and
+    the exact A8 route on a token sample of the M = 2048 projection; plus one
+    layer of the 64-layer decode step at M = 5 (its five projections),
+    extrapolated to the whole step."""
     from oracle import a8, q4
     try:
         from threadpoolctl import threadpool_limits
     except Exception:
         threadpool_limits = None
     threads = _blas_threads()
+
+    def both(fn):
+        """(reps, seconds) with all threads, and with one thread (or None)."""
+        r = _timed_calls(fn, budget_s)
+        if threadpool_limits is None:
+            return r, None
+        with threadpool_limits(limits=1):
+            return r, _timed_calls(fn, budget_s)
+
     out = {}
     # headline: decode_gate_up, M = 1
     wl = synthetic.WORKLOADS["decode_gate_up"]
@@ -469,16 +480,14 @@ def cpu_baseline(synthetic, budget_s=4.0):
     del w
     x = synthetic.activations(m, k, synthetic.ACT_SEED)
     b = gemv_bytes(m, k, n)
-    reps, el = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
+    (reps, el), one = both(lambda: q4.matmul(x, q, d))
     out.update(value=b * reps / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
                sample=f"oracle q4.matmul (dequantize to fp64, then fp64 matvec) on the full "
                       f"decode_gate_up matrix M={m} K={k} N={n}, {reps} calls in {el:.1f} s; "
                       f"{threads} BLAS threads; host has {os.cpu_count()} logical CPUs")
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=1):
-            reps1, el1 = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
-        out["single_thread"] = dict(value=b * reps1 / el1 / 1e9, unit="GB/s", cores=1,
-                                    sample=f"same, {reps1} calls in {el1:.1f} s, 1 BLAS thread")
+    if one:
+        out["single_thread"] = dict(value=b * one[0] / one[1] / 1e9, unit="GB/s", cores=1,
+                                    sample=f"same, {one[0]} calls in {one[1]:.1f} s, 1 BLAS thread")
     del q, d
     # verify down-projection, M = 5 (K = 17408, N = 5120)
     wl = synthetic.WORKLOADS["verify_down"]
@@ -487,9 +496,13 @@ def cpu_baseline(synthetic, budget_s=4.0):
     q, d = q4.quantize(w)
     del w
     x = synthetic.activations(m, k, synthetic.ACT_SEED)
-    reps, el = _timed_calls(lambda: q4.matmul(x, q, d), budget_s)
-    out["verify_down_m5"] = dict(value=gemv_bytes(m, k, n) * reps / el / 1e9, unit="GB/s", cores=int(threads),
+    b = gemv_bytes(m, k, n)
+    (reps, el), one = both(lambda: q4.matmul(x, q, d))
+    out["verify_down_m5"] = dict(value=b * reps / el / 1e9, unit="GB/s", cores=int(threads),
                                  sample=f"q4.matmul M={m} K={k} N={n}, {reps} calls in {el:.1f} s")
+    if one:
+        out["verify_down_m5"]["single_thread"] = dict(value=b * one[0] / one[1] / 1e9, unit="GB/s", cores=1,
+                                                      sample=f"same, {one[0]} calls in {one[1]:.1f} s")
     del q, d
     # A8 route, M = 2048, K = 5120, N = 17408: the exact oracle on 64 of the tokens
     wl = synthetic.WORKLOADS["prefill_a8"]
@@ -499,12 +512,35 @@ def cpu_baseline(synthetic, budget_s=4.0):
     del w
     tokens = 64
     x = synthetic.activations(tokens, k, synthetic.ACT_SEED)
-    reps, el = _timed_calls(lambda: a8.prefill(x, q, d), budget_s)
+    (reps, el), one = both(lambda: a8.prefill(x, q, d))
     out["a8_prefill"] = dict(value=tokens * reps / el, unit="tokens/s", cores=int(threads),
                              tops=2 * tokens * n * k * reps / el / 1e12,
                              sample=f"a8.prefill (int8 quantization, 160 fp64 K=32 GEMMs of exact block "
                                     f"sums, fp64 rescale) on {tokens} tokens x K={k} x N={n}, "
                                     f"{reps} calls in {el:.1f} s")
+    if one:
+        out["a8_prefill"]["single_thread"] = dict(value=tokens * one[0] / one[1], unit="tokens/s", cores=1,
+                                                  tops=2 * tokens * n * k * one[0] / one[1] / 1e12,
+                                                  sample=f"same, {one[0]} calls in {one[1]:.1f} s")
+    del q, d
+    # decode step, M = 5: layer 0's five projections, one at a time, scaled to 64 layers
+    m = 5
+    layer = []
+    for pi, (_, k, n) in enumerate(synthetic.LAYER_PROJECTIONS):
+        w = synthetic.weights(n, k, synthetic.layer_weight_seed(0, pi))
+        q, d = q4.quantize(w)
+        del w
+        layer.append((synthetic.activations(m, k, synthetic.ACT_SEED), q, d))
+    step_layer = lambda: [q4.matmul(x, q, d) for x, q, d in layer]
+    reps, el = _timed_calls(step_layer, budget_s)
+    t_layer = el / reps
+    wbytes = sum(int(n * k * BYTES_PER_WEIGHT) for _, k, n in synthetic.LAYER_PROJECTIONS) * synthetic.N_LAYERS
+    out["decode_step_m5"] = dict(value=wbytes / (t_layer * synthetic.N_LAYERS) / 1e9, unit="GB/s",
+                                 cores=int(threads), ms_per_step=t_layer * synthetic.N_LAYERS * 1e3,
+                                 sample=f"q4.matmul over layer 0's five projections at M={m} "
+                                        f"(qkv, out, gate, up, down), {reps} layer passes in {el:.1f} s, "
+                                        f"times {synthetic.N_LAYERS} layers")
+    del layer
     return out
 
 
