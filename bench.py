@@ -166,11 +166,15 @@ def bench_decode(torch, q4w, synthetic, steps, warmup):
     ws = torch.zeros(max(q4w.gemv_ws_bytes(m, n, k, 0), 1), dtype=torch.uint8, device="cuda")
     warm_clocks(torch, lambda: [q4w.q4_gemv_skinny_raw(x, c, s, y, 0, ws) for c, s in copies])
     ts, tg = gemv_series(torch, q4w, copies, x, y, steps, warmup)
+    # two more series of the same `steps` stream launches, for the spread (the
+    # line's value is the first series)
+    more = [gemv_series(torch, q4w, copies, x, y, steps, 0)[0] for _ in range(2)]
     b = gemv_bytes(m, k, n)
     out = dict(M=m, K=k, N=n, copies=len(copies), bytes_per_launch=b,
                t_stream_s=ts, t_graph_s=tg,
                gbs_stream=b * steps / ts / 1e9, gbs_graph=b * steps / tg / 1e9,
-               us_per_launch_stream=ts / steps * 1e6, us_per_launch_graph=tg / steps * 1e6)
+               us_per_launch_stream=ts / steps * 1e6, us_per_launch_graph=tg / steps * 1e6,
+               us_per_launch_series=[t / steps * 1e6 for t in [ts] + more])
     del copies
     torch.cuda.empty_cache()
     return out
@@ -704,6 +708,7 @@ def main():
         "graph": {"gbs": round(dec["gbs_graph"], 2), "us_per_launch": round(dec["us_per_launch_graph"], 3),
                   "note": "the same K launches as one HIP graph replay, which adds a fixed cost per replay"},
         "us_per_launch": round(dec["us_per_launch_stream"], 3),
+        "us_per_launch_series": [round(t, 3) for t in dec["us_per_launch_series"]],
         "kernel_source_hash": kernel_source_hash(),
     }
     result.update(extra)
