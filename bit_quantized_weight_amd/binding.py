@@ -377,14 +377,15 @@ def batched_plan(items):
 
 def stream_read(buf, grid=256, block=512, out=None):
     """Plain streaming read of a device tensor's bytes (a measurement helper):
-    returns out, int32 [grid], each workgroup's XOR of the words it read."""
+    returns out, int32 [grid * block / 64], each wave's XOR of the words it read."""
     import torch
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous CUDA tensor")
+    nout = grid * (block // 64)
     if out is None:
-        out = torch.empty(grid, dtype=torch.int32, device=buf.device)
+        out = torch.empty(nout, dtype=torch.int32, device=buf.device)
     _need(out, torch.int32, "out")
-    _need_shape(out, (grid,), "out")
+    _need_shape(out, (nout,), "out")
     nbytes = buf.numel() * buf.element_size()
     _check("q4w_stream_read", lib().q4w_stream_read(_ptr(buf), nbytes, _ptr(out), grid, block, _stream()))
     return out

@@ -4,8 +4,9 @@
 //
 // Every thread keeps four 16-byte loads in flight, grid-stride over the
 // buffer, so at any time the whole chip reads one narrow window of it; each
-// workgroup writes the XOR of the 32-bit words it read (a checksum, which
-// also keeps the loads from being optimized away).
+// wave writes the XOR of the 32-bit words it read (a checksum, which also
+// keeps the loads from being optimized away), reduced in registers so that
+// the launch ends without LDS round trips or a barrier.
 
 #include "q4w_internal.h"
 
@@ -15,7 +16,6 @@ namespace {
 constexpr int kReadUnroll = 4;
 
 __global__ void stream_read_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* __restrict__ out) {
-  __shared__ uint32_t part[16];
   const size_t nthreads = (size_t)gridDim.x * blockDim.x;
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t x = 0;
@@ -29,17 +29,17 @@ __global__ void stream_read_kernel(const uint4* __restrict__ p, size_t n16, uint
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  // XOR over the wave, then over the workgroup's waves
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) part[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) r ^= part[w];
-    out[blockIdx.x] = r;
-  }
+  // XOR over the wave in registers (no LDS round trips, no barrier): rotations
+  // within each row of 16 lanes, then across rows (lanes l ^ 16, l ^ 32).
+  x ^= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
+  x ^= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);   // row_ror:4
+  x ^= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);   // row_ror:2
+  x ^= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);   // row_ror:1
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = r16[0] ^ r16[1];
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = r32[0] ^ r32[1];
+  if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = x;
 }
 
 }  // namespace

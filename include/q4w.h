@@ -297,9 +297,10 @@ int q4_gemv_batched_run(const q4w_batched_plan* plan, hipStream_t stream);
  *   (the whole chip reads one narrow window of the buffer at a time).  It
  *   gives the read rate this GPU reaches for a given launch shape, the
  *   achievable ceiling that the HBM-bound kernels above are measured against
- *   (next to the published 8 TB/s peak).  out[w] (uint32, `grid` entries) is
- *   the XOR of the 32-bit words that workgroup w read, a checksum: the XOR of
- *   out[0 .. grid) is the XOR of every word of the buffer.
+ *   (next to the published 8 TB/s peak).  out (uint32, grid * block / 64
+ *   entries, one per wave): out[w * (block / 64) + v] is the XOR of the 32-bit
+ *   words that wave v of workgroup w read, a checksum: the XOR of all entries
+ *   is the XOR of every word of the buffer.
  *   buf 16-byte aligned (may be NULL when bytes == 0), bytes % 16 == 0 (else
  *   UNSUPPORTED_SHAPE), out 4-byte aligned, 1 <= grid <= 65536,
  *   64 <= block <= 1024 with block % 64 == 0 (else INVALID_ARG).

@@ -20,6 +20,7 @@ def test_checksum(nbytes, grid, block):
     buf = torch.from_numpy(data.view(np.int32)).to("cuda") if nbytes else torch.empty(0, dtype=torch.int32, device="cuda")
     out = stream_read(buf, grid=grid, block=block)
     torch.cuda.synchronize()
-    got = np.bitwise_xor.reduce(host(out).view(np.uint32)) if grid > 1 else host(out).view(np.uint32)[0]
+    assert out.shape == (grid * (block // 64),)
+    got = np.bitwise_xor.reduce(host(out).view(np.uint32))
     want = np.bitwise_xor.reduce(data) if nbytes else np.uint32(0)
     assert int(got) == int(want)
