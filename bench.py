@@ -189,6 +189,9 @@ def bench_verify(torch, q4w, synthetic, steps, warmup):
         # median of three timed graph replays of `steps` launches (min and max kept)
         x = synthetic.activations_device(m, k, synthetic.ACT_SEED)
         y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        # the previous M's graph capture left the GPU idle: warm the clock first
+        ws = torch.zeros(max(q4w.gemv_ws_bytes(m, n, k, 0), 1), dtype=torch.uint8, device="cuda")
+        warm_clocks(torch, lambda: [q4w.q4_gemv_skinny_raw(x, c, s, y, 0, ws) for c, s in copies])
         t, tg, ts = gemv_series(torch, q4w, copies, x, y, steps, warmup, series=3)
         b = gemv_bytes(m, k, n)
         res[str(m)] = dict(gbs=b * steps / t / 1e9, us_per_launch=t / steps * 1e6,
