@@ -366,8 +366,7 @@ def bench_ceiling(torch, q4w, reps=40):
                 for i in range(n):
                     q4w.stream_read(views[i % len(views)], grid, block, out)
 
-            if best is None:
-                warm_clocks(torch, run)
+            warm_clocks(torch, run)
             dt_stream = time_region(torch, run, preroll=run) / n
             # Launched from Python, a ~9 us read of 50 MB is bounded by the host's
             # enqueue rate (about 10 us per call through the binding); one HIP
